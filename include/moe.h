@@ -1,0 +1,166 @@
+/*
+ * moe.h - C ABI of libmoe_decode.so, an MI355X (gfx950) implementation of
+ * the memory-bound decode step of a sparse Mixture-of-Experts layer.
+ *
+ * The step follows the Kimi K3 decode pages: each token picks 16 of 896
+ * routed experts (page "英伟达用1.2万行CuTe DSL Megakernel，如何优化Kimi K3？",
+ * section "一个工程师、1.2万行代码、AI辅助开发"; tmtpost page, section "现象"),
+ * expert weights are MXFP4 (tmtpost page, section "现象"), a shared expert is
+ * always active beside the routed ones (page "AI手搓1.2万行代码榨干GB300!…",
+ * section 02; smzdm page, section "四步改造"), and the layer ends with the
+ * residual add (smzdm page, section "慢的根源").  The fast path is limited to
+ * small batches (up to 64 tokens), as the pages' latency path is (page
+ * "AI手搓1.2万行代码榨干GB300!…", section 03).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All pointers named in a struct or argument are DEVICE pointers unless
+ *    the comment says "host".  The caller owns every buffer; the library
+ *    never allocates, frees or synchronises and keeps no global state.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *    Calls are safe to capture into a HIP graph: no host read-back, no
+ *    allocation, no memset nodes.
+ *  - Every argument is validated on the host before anything is enqueued;
+ *    on error nothing is enqueued and a negative moe_status is returned.
+ *    Kernel faults surface at the caller's next synchronisation.
+ *  - bf16 values are passed as uint16_t bit patterns.
+ *  - MXFP4 matrix M[R][C] (OCP Microscaling v1.0: E2M1 elements, one E8M0
+ *    scale 2^(b-127) per 32 consecutive elements of a row, b = 0xFF is NaN):
+ *      codes  uint8 [R][C/2]  element 2i in bits 3:0 of byte i, 2i+1 in 7:4
+ *      scales uint8 [R][C/32]
+ *    codes must be 16-byte aligned.  The reduction dimension is the row:
+ *    C = H for gate/up, C = F for down.
+ *  - Workspace: `ws` is a 16-byte aligned device buffer of at least
+ *    moe_workspace_size() bytes.  Its first MOE_WS_COUNTER_BYTES bytes hold
+ *    completion counters that must be zero before the first call
+ *    (moe_workspace_init() zero-fills the whole buffer); every call leaves
+ *    them at zero again, so one workspace serves any number of calls.  The
+ *    rest is scratch that each call writes before it reads it.  Calls that
+ *    overlap in time (different streams) need different workspaces.
+ *  - Expert indices read from device memory (topk_idx arguments, or the
+ *    router's own output) are clamped to [0, E) before addressing weights;
+ *    an out-of-range index gives unspecified values for that slot, never an
+ *    out-of-bounds access.
+ *
+ * Limits (MOE_ERR_UNSUPPORTED beyond them)
+ *    0 <= T <= 64 tokens (T = 0 is a no-op returning MOE_OK)
+ *    H % 256 == 0, 256 <= H <= 8192, and (H/256)/gcd(H/256, 4) <= 8
+ *      (every multiple of 256 up to 2048, and e.g. 3072, 4096, 7168, 8192)
+ *    F % 128 == 0 and F/32/gcd(F/32, 64) <= 2
+ *      (F in {128, 256, 512, 1024, 2048, 4096})
+ *    1 <= k <= min(E, 32), 1 <= E <= 1024
+ *    n_shared in {0, 1}; with a shared expert, shared_ffn == ffn
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_WS_COUNTER_BYTES 256
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad value, aliasing */
+  MOE_ERR_UNSUPPORTED = -2, /* well-formed but outside the limits above */
+  MOE_ERR_WORKSPACE = -3,   /* ws null or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = -4          /* a HIP launch failed */
+} moe_status;
+
+typedef struct {
+  int32_t hidden;     /* H */
+  int32_t n_experts;  /* E, routed experts */
+  int32_t top_k;      /* k, routed experts used per token */
+  int32_t ffn;        /* F, width of each routed expert */
+  int32_t n_shared;   /* S in {0, 1} */
+  int32_t shared_ffn; /* Fs (== F when S = 1) */
+} moe_shape;
+
+typedef struct {
+  const uint8_t* codes;  /* [R][C/2], 16-byte aligned */
+  const uint8_t* scales; /* [R][C/32] */
+} moe_mx_mat;
+
+typedef struct {
+  const uint16_t* router_w; /* bf16 [E][H], 16-byte aligned */
+  moe_mx_mat gate;          /* routed, expert-major [E][F][H] */
+  moe_mx_mat up;            /* routed, expert-major [E][F][H] */
+  moe_mx_mat down;          /* routed, expert-major [E][H][F] */
+  moe_mx_mat s_gate;        /* shared [Fs][H]; ignored when n_shared == 0 */
+  moe_mx_mat s_up;          /* shared [Fs][H] */
+  moe_mx_mat s_down;        /* shared [H][Fs] */
+} moe_layer_weights;
+
+/* Workspace bytes needed for calls with up to `max_tokens` tokens.
+ * Returns MOE_OK and writes *bytes (host pointer). */
+int moe_workspace_size(const moe_shape* shape, int32_t max_tokens, size_t* bytes);
+
+/* Zero-fill a workspace (a fill kernel, not a memset node). */
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Router GEMV and top-k selection.
+ *   l[t][e] = sum_h x[t][h] * Wr[e][h]  (fp32 accumulation of exact bf16
+ *   products); the k largest logits per token ordered by (logit desc,
+ *   expert index asc), -0 treated as +0; weights = softmax over those k.
+ * x        bf16 [T][H], 16-byte aligned
+ * router_w bf16 [E][H], 16-byte aligned
+ * topk_idx int32 [T][k] out;  topk_w fp32 [T][k] out (sums to 1 per token)
+ * logits   fp32 [T][E] out, may be NULL */
+int moe_router_topk(const moe_shape* shape, const uint16_t* x, const uint16_t* router_w,
+                    int32_t n_tokens, int32_t* topk_idx, float* topk_w, float* logits,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Gate/up projections of the selected experts with SiLU gating:
+ *   act[t][j][f] = silu(G_e x_t)[f] * (U_e x_t)[f],  e = topk_idx[t][j]
+ * computed in fp32 from the MXFP4 weights (dequantised in the dot product).
+ * topk_idx int32 [T][k] (device), act fp32 [T][k][F] out.
+ * This is the layer's dominant HBM stream, exported for measurement. */
+int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
+                      const int32_t* topk_idx, int32_t n_tokens, float* act,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* One MoE decode layer:
+ *   out[t] = residual[t] + sum_j topk_w[t][j] * y_{idx[t][j]}(x_t) + y_shared(x_t)
+ *   y_e(x) = D_e (silu(G_e x) * (U_e x)), shared expert weight 1
+ * rounded once to bf16 (nearest even).
+ * x        bf16 [T][H]
+ * residual bf16 [T][H] or NULL (no residual); may equal x
+ * out      bf16 [T][H]; may equal residual, must not overlap x otherwise
+ * topk_idx_out int32 [T][k] / topk_w_out fp32 [T][k]: optional copies */
+int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
+                     const uint16_t* residual, uint16_t* out, int32_t n_tokens,
+                     int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* A stack of decode layers run back to back.  Per layer l:
+ *   xn = bf16(h * gamma_l / sqrt(mean(h^2) + eps));  h = bf16(h + MoE_l(xn))
+ * layers  host array [n_layers] of weight sets (read during the call only)
+ * gammas  host array [n_layers] of device bf16 [H] pointers
+ * hidden  bf16 [T][H], input h_0 and output h_L (updated in place)
+ * topk_idx_out  int32 [n_layers][T][k] or NULL
+ * hidden_trace  bf16 [n_layers][T][H] or NULL: h after each layer */
+int moe_decode_stack(const moe_shape* shape, const moe_layer_weights* layers,
+                     const uint16_t* const* gammas, float eps, int32_t n_layers,
+                     uint16_t* hidden, int32_t n_tokens, int32_t* topk_idx_out,
+                     uint16_t* hidden_trace, void* ws, size_t ws_bytes, void* stream);
+
+/* Token grouping used by the batched path: a stable counting sort of the
+ * T*k (token, slot) pairs by expert.
+ *   offsets int32 [E+1] out: pairs of expert e are pairs[offsets[e]..offsets[e+1])
+ *   pairs   int32 [T*k] out: t*k + j, increasing within each expert */
+int moe_group_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t top_k,
+                        int32_t n_experts, int32_t* offsets, int32_t* pairs,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

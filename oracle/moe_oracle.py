@@ -228,14 +228,16 @@ def group_by_expert(idx: np.ndarray, n_experts: int):
     return offsets, pairs
 
 
-def moe_layer(x_bits, router_w_bits, k, routed, shared=None, residual_bits=None):
+def moe_layer(x_bits, router_w_bits, k, routed, shared=None, residual_bits=None, pmap=map):
     """One MoE decode layer in float64.
 
     ``x_bits``: bf16 ``[T][H]``; ``router_w_bits``: bf16 ``[E][H]``;
     ``routed(e)`` returns expert e as ``{"gate": (codes, scales), "up": ...,
     "down": ...}``; ``shared`` is such a dict or None; ``residual_bits`` is
-    bf16 ``[T][H]`` or None (no residual).  Returns a dict with ``out``
-    (float64 ``[T][H]``), ``idx``, ``w``, ``logits``.
+    bf16 ``[T][H]`` or None (no residual).  ``pmap`` evaluates the
+    independent expert outputs (e.g. a thread pool's map); the weighted sum
+    is always taken in slot order.  Returns a dict with ``out`` (float64
+    ``[T][H]``), ``idx``, ``w``, ``logits``.
     """
     x_bits = np.atleast_2d(x_bits)
     T, H = x_bits.shape
@@ -244,16 +246,16 @@ def moe_layer(x_bits, router_w_bits, k, routed, shared=None, residual_bits=None)
     w = topk_weights(logits, idx)
     x = bf16_to_f64(x_bits)
     out = np.zeros((T, H)) if residual_bits is None else bf16_to_f64(np.atleast_2d(residual_bits)).copy()
-    cache = {}
     for t in range(T):
+        jobs = [(x[t], int(e)) for e in idx[t]]
+        if shared is not None:
+            jobs.append((x[t], -1))
+        ys = list(pmap(lambda job: expert_ffn(job[0], shared if job[1] < 0 else routed(job[1])), jobs))
         acc = np.zeros(H)
         for j in range(k):
-            e = int(idx[t, j])
-            if e not in cache:
-                cache[e] = routed(e)
-            acc += w[t, j] * expert_ffn(x[t], cache[e])
+            acc += w[t, j] * ys[j]
         if shared is not None:
-            acc += expert_ffn(x[t], shared)
+            acc += ys[k]
         out[t] += acc
     return {"out": out, "idx": idx, "w": w, "logits": logits}
 
@@ -269,7 +271,7 @@ def rmsnorm_bf16(h_bits: np.ndarray, gamma_bits: np.ndarray, eps: float) -> np.n
     return f64_to_bf16(h * g / r)
 
 
-def moe_stack(h_bits, layers, eps, teacher=None):
+def moe_stack(h_bits, layers, eps, teacher=None, pmap=map):
     """Layers run back to back: RMSNorm, MoE layer, residual add, bf16 round.
 
     ``layers``: list of dicts with ``router`` (bf16 [E][H]), ``gamma``
@@ -284,7 +286,7 @@ def moe_stack(h_bits, layers, eps, teacher=None):
         if teacher is not None:
             h = np.atleast_2d(teacher[li])
         xn = rmsnorm_bf16(h, L["gamma"], eps)
-        r = moe_layer(xn, L["router"], L["k"], L["routed"], L["shared"], residual_bits=h)
+        r = moe_layer(xn, L["router"], L["k"], L["routed"], L["shared"], residual_bits=h, pmap=pmap)
         h_next = f64_to_bf16(r["out"])
         recs.append({"h": h, "xn": xn, "idx": r["idx"], "w": r["w"],
                      "logits": r["logits"], "out": r["out"], "h_next": h_next})

@@ -1,0 +1,268 @@
+// C ABI of the MoE decode library: host-side validation, workspace layout
+// and kernel sequencing.  Semantics of every entry point are documented in
+// include/moe.h.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <numeric>
+
+#include "moe_internal.h"
+
+namespace {
+
+using moe::LayerT1;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+  size_t ticket, logits, idx, wts, act, y_shared, xn, group, total;
+};
+
+WsLayout ws_layout(const moe_shape& s, int T) {
+  WsLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  const size_t nslot = (size_t)s.top_k + (size_t)s.n_shared;
+  L.ticket = take(kAlign);
+  L.logits = take(sizeof(float) * (size_t)T * s.n_experts);
+  L.idx = take(sizeof(int32_t) * (size_t)T * s.top_k);
+  L.wts = take(sizeof(float) * (size_t)T * s.top_k);
+  L.act = take(sizeof(float) * (size_t)T * nslot * s.ffn);
+  L.y_shared = take(sizeof(float) * (size_t)T * s.hidden);
+  L.xn = take(sizeof(uint16_t) * (size_t)T * s.hidden);
+  L.group = take(sizeof(int32_t) * (size_t)(s.n_experts + 1 + T * s.top_k));
+  L.total = o;
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Structural validation of a shape (no pointers).
+int check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->hidden <= 0 || s->n_experts <= 0 || s->top_k <= 0 || s->ffn <= 0 || s->n_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->top_k > s->n_experts) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared > 1) return MOE_ERR_UNSUPPORTED;
+  if (s->n_shared == 1 && s->shared_ffn != s->ffn) return MOE_ERR_UNSUPPORTED;
+  if (s->n_experts > moe::kMaxExperts || s->top_k > moe::kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (s->hidden % 256 || s->hidden > 8192) return MOE_ERR_UNSUPPORTED;
+  if (moe::gateup_map(s->hidden).bpl > moe::kMaxBplGateUp) return MOE_ERR_UNSUPPORTED;
+  if (s->ffn % 128) return MOE_ERR_UNSUPPORTED;
+  if (moe::down_map(s->ffn).bpl > moe::kMaxBplDown) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_tokens(int32_t T) {
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > moe::kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_ws(const moe_shape* s, int32_t T, const void* ws, size_t ws_bytes) {
+  if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  if (ws_layout(*s, T).total > ws_bytes) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+int check_mat(const moe_mx_mat& m) {
+  if (!m.codes || !m.scales || !aligned16(m.codes)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int check_weights(const moe_shape* s, const moe_layer_weights* w, bool need_router) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (need_router && (!w->router_w || !aligned16(w->router_w))) return MOE_ERR_INVALID_ARG;
+  int rc;
+  if ((rc = check_mat(w->gate)) || (rc = check_mat(w->up)) || (rc = check_mat(w->down))) return rc;
+  if (s->n_shared &&
+      ((rc = check_mat(w->s_gate)) || (rc = check_mat(w->s_up)) || (rc = check_mat(w->s_down))))
+    return rc;
+  return MOE_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+LayerT1 make_layer(const moe_shape* s, const moe_layer_weights* w, void* ws) {
+  const WsLayout W = ws_layout(*s, 1);
+  char* b = (char*)ws;
+  LayerT1 L{};
+  L.H = s->hidden;
+  L.E = s->n_experts;
+  L.k = s->top_k;
+  L.F = s->ffn;
+  L.S = s->n_shared;
+  if (w) {
+    L.router_w = w->router_w;
+    L.g_codes = w->gate.codes;
+    L.g_scales = w->gate.scales;
+    L.u_codes = w->up.codes;
+    L.u_scales = w->up.scales;
+    L.d_codes = w->down.codes;
+    L.d_scales = w->down.scales;
+    if (s->n_shared) {
+      L.sg_codes = w->s_gate.codes;
+      L.sg_scales = w->s_gate.scales;
+      L.su_codes = w->s_up.codes;
+      L.su_scales = w->s_up.scales;
+      L.sd_codes = w->s_down.codes;
+      L.sd_scales = w->s_down.scales;
+    }
+  }
+  L.ticket = (unsigned*)(b + W.ticket);
+  L.logits = (float*)(b + W.logits);
+  L.idx = (int32_t*)(b + W.idx);
+  L.wts = (float*)(b + W.wts);
+  L.act = (float*)(b + W.act);
+  L.y_shared = (float*)(b + W.y_shared);
+  L.xn = (uint16_t*)(b + W.xn);
+  return L;
+}
+
+// One full single-token layer: K1, K2, K3 on one stream.
+int run_layer_t1(LayerT1& L, hipStream_t st) {
+  hipError_t e = moe::launch_router_topk_t1(L, true, st);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const uint16_t* xin = L.gamma ? L.xn : L.x;
+  e = moe::launch_gateup_t1(L, xin, L.idx, L.act, true, st);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_down_combine_t1(L, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or size";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int moe_workspace_size(const moe_shape* shape, int32_t max_tokens, size_t* bytes) {
+  int rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens(max_tokens))) return rc;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = ws_layout(*shape, max_tokens < 1 ? 1 : max_tokens).total;
+  return MOE_OK;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_zero_fill(ws, ws_bytes & ~(size_t)3, (hipStream_t)stream));
+}
+
+int moe_router_topk(const moe_shape* shape, const uint16_t* x, const uint16_t* router_w,
+                    int32_t n_tokens, int32_t* topk_idx, float* topk_w, float* logits, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
+  if (n_tokens == 0) return MOE_OK;
+  if (!x || !aligned16(x) || !router_w || !aligned16(router_w) || !topk_idx || !topk_w)
+    return MOE_ERR_INVALID_ARG;
+  if ((rc = check_ws(shape, n_tokens, ws, ws_bytes))) return rc;
+  if (n_tokens > 1) return MOE_ERR_UNSUPPORTED;
+  LayerT1 L = make_layer(shape, nullptr, ws);
+  L.router_w = router_w;
+  L.x = x;
+  L.idx_out = topk_idx;
+  L.w_out = topk_w;
+  L.logits_out = logits;
+  return hip_status(moe::launch_router_topk_t1(L, false, (hipStream_t)stream));
+}
+
+int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
+                      const int32_t* topk_idx, int32_t n_tokens, float* act, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
+  if (n_tokens == 0) return MOE_OK;
+  if ((rc = check_weights(shape, w, false))) return rc;
+  if (!x || !aligned16(x) || !topk_idx || !act) return MOE_ERR_INVALID_ARG;
+  if ((rc = check_ws(shape, n_tokens, ws, ws_bytes))) return rc;
+  if (n_tokens > 1) return MOE_ERR_UNSUPPORTED;
+  LayerT1 L = make_layer(shape, w, ws);
+  return hip_status(moe::launch_gateup_t1(L, x, topk_idx, act, false, (hipStream_t)stream));
+}
+
+int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
+                     const uint16_t* residual, uint16_t* out, int32_t n_tokens,
+                     int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
+  if (n_tokens == 0) return MOE_OK;
+  if ((rc = check_weights(shape, w, true))) return rc;
+  if (!x || !aligned16(x) || !out) return MOE_ERR_INVALID_ARG;
+  const size_t vec = sizeof(uint16_t) * (size_t)n_tokens * shape->hidden;
+  if (residual != x && overlaps(out, vec, x, vec)) return MOE_ERR_INVALID_ARG;
+  if (residual && residual != out && overlaps(out, vec, residual, vec)) return MOE_ERR_INVALID_ARG;
+  if ((rc = check_ws(shape, n_tokens, ws, ws_bytes))) return rc;
+  if (overlaps(ws, ws_bytes, out, vec) || overlaps(ws, ws_bytes, x, vec)) return MOE_ERR_INVALID_ARG;
+  if (n_tokens > 1) return MOE_ERR_UNSUPPORTED;
+  LayerT1 L = make_layer(shape, w, ws);
+  L.x = x;
+  L.residual = residual;
+  L.out = out;
+  L.idx_out = topk_idx_out;
+  L.w_out = topk_w_out;
+  return run_layer_t1(L, (hipStream_t)stream);
+}
+
+int moe_decode_stack(const moe_shape* shape, const moe_layer_weights* layers,
+                     const uint16_t* const* gammas, float eps, int32_t n_layers, uint16_t* hidden,
+                     int32_t n_tokens, int32_t* topk_idx_out, uint16_t* hidden_trace, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
+  if (n_layers < 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (n_tokens == 0 || n_layers == 0) return MOE_OK;
+  if (!layers || !gammas || !hidden || !aligned16(hidden)) return MOE_ERR_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((rc = check_weights(shape, &layers[l], true))) return rc;
+    if (!gammas[l] || !aligned16(gammas[l])) return MOE_ERR_INVALID_ARG;
+  }
+  if ((rc = check_ws(shape, n_tokens, ws, ws_bytes))) return rc;
+  const size_t vec = sizeof(uint16_t) * (size_t)n_tokens * shape->hidden;
+  if (overlaps(ws, ws_bytes, hidden, vec)) return MOE_ERR_INVALID_ARG;
+  if (n_tokens > 1) return MOE_ERR_UNSUPPORTED;
+  const hipStream_t st = (hipStream_t)stream;
+  for (int l = 0; l < n_layers; ++l) {
+    LayerT1 L = make_layer(shape, &layers[l], ws);
+    L.x = hidden;
+    L.gamma = gammas[l];
+    L.eps = eps;
+    L.residual = hidden;
+    L.out = hidden;
+    L.trace = hidden_trace ? hidden_trace + (size_t)l * n_tokens * shape->hidden : nullptr;
+    L.idx_out = topk_idx_out ? topk_idx_out + (size_t)l * n_tokens * shape->top_k : nullptr;
+    if ((rc = run_layer_t1(L, st))) return rc;
+  }
+  return MOE_OK;
+}
+
+int moe_group_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t top_k,
+                        int32_t n_experts, int32_t* offsets, int32_t* pairs, void* ws,
+                        size_t ws_bytes, void* stream) {
+  (void)topk_idx; (void)n_tokens; (void)top_k; (void)n_experts; (void)offsets; (void)pairs;
+  (void)ws; (void)ws_bytes; (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

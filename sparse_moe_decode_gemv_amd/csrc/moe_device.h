@@ -1,0 +1,120 @@
+// Device-side helpers of the gfx950 MoE decode kernels.
+//
+// MXFP4 blocks (OCP Microscaling v1.0) are 16 code bytes (32 E2M1 elements,
+// element 2i in the low nibble of byte i) sharing one E8M0 scale byte.  The
+// hot loops turn code bytes into exact bf16 or fp32 element pairs with the
+// CDNA4 conversion instructions and fold the power-of-two block scale in
+// once per block, in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// E8M0 byte -> fp32 2^(b-127) (exact; denormal for b = 0); 0xFF is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  const float s = __builtin_amdgcn_ldexpf(1.0f, (int)b - 127);
+  return b == 0xFFu ? __uint_as_float(0x7FC00000u) : s;
+}
+
+// bf16 pair view of a dword (element 2i in the low half).
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) {
+  return __builtin_bit_cast(bf16x2, v);
+}
+
+// Dot product of one 32-element MXFP4 block (4 code dwords, scale not
+// applied) with 32 bf16 activations (16 dwords, pairs in element order).
+__device__ __forceinline__ float block_dot_bf16(const uint4 c, const uint32_t* xv) {
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[d], 1.0f, 0);
+    bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[d], 1.0f, 1);
+    bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[d], 1.0f, 2);
+    bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[d], 1.0f, 3);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(w0, as_bf16x2(xv[4 * d + 0]), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(w1, as_bf16x2(xv[4 * d + 1]), a1, false);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(w2, as_bf16x2(xv[4 * d + 2]), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(w3, as_bf16x2(xv[4 * d + 3]), a1, false);
+  }
+  return a0 + a1;
+}
+
+// Dot product of one 32-element MXFP4 block with 32 fp32 activations.
+__device__ __forceinline__ float block_dot_f32(const uint4 c, const float* av) {
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const f32x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[d], 1.0f, 0);
+    const f32x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[d], 1.0f, 1);
+    const f32x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[d], 1.0f, 2);
+    const f32x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[d], 1.0f, 3);
+    const float* a = av + 8 * d;
+    a0 = __builtin_fmaf(w0.x, a[0], a0);
+    a1 = __builtin_fmaf(w0.y, a[1], a1);
+    a0 = __builtin_fmaf(w1.x, a[2], a0);
+    a1 = __builtin_fmaf(w1.y, a[3], a1);
+    a0 = __builtin_fmaf(w2.x, a[4], a0);
+    a1 = __builtin_fmaf(w2.y, a[5], a1);
+    a0 = __builtin_fmaf(w3.x, a[6], a0);
+    a1 = __builtin_fmaf(w3.y, a[7], a1);
+  }
+  return a0 + a1;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Order-preserving 32-bit key of an fp32 value (-0 folded onto +0), so that
+// unsigned comparison of keys orders the values.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Agent-scope release/acquire fences (all XCDs of the device).
+__device__ __forceinline__ void fence_release_agent() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+}
+__device__ __forceinline__ void fence_acquire_agent() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+}  // namespace moe

@@ -1,0 +1,73 @@
+// Internal launch interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Lane mapping of a row-streaming GEMV over MXFP4 rows of `nblk` 32-element
+// blocks: `lanes` lanes share a row and each handles `bpl` blocks strided by
+// `lanes`, so one wave covers 64/lanes rows per load instruction.
+struct RowMap {
+  int lanes;
+  int bpl;
+};
+
+// gate/up rows (reduction over H): a half wave (32 lanes) per matrix.
+inline RowMap gateup_map(int H) {
+  int nb = H / 32, g = 32;
+  while (nb % g) g >>= 1;
+  return {g, nb / g};
+}
+// down rows (reduction over F): the whole wave.
+inline RowMap down_map(int F) {
+  int nb = F / 32, g = 64;
+  while (nb % g) g >>= 1;
+  return {g, nb / g};
+}
+
+constexpr int kMaxBplGateUp = 8;
+constexpr int kMaxBplDown = 2;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxTokens = 64;
+
+// ---- T = 1 path ------------------------------------------------------------
+
+struct LayerT1 {
+  int H, E, k, F, S;
+  // inputs
+  const uint16_t* x;         // bf16 [H]: layer input, or h when gamma != null
+  const uint16_t* gamma;     // RMSNorm gain (stack) or null
+  float eps;
+  const uint16_t* residual;  // bf16 [H] or null
+  uint16_t* out;             // bf16 [H]
+  uint16_t* trace;           // optional copy of out
+  // weights
+  const uint16_t* router_w;
+  const uint8_t *g_codes, *g_scales, *u_codes, *u_scales, *d_codes, *d_scales;
+  const uint8_t *sg_codes, *sg_scales, *su_codes, *su_scales, *sd_codes, *sd_scales;
+  // workspace
+  float* logits;       // [E]
+  int32_t* idx;        // [k]
+  float* wts;          // [k]
+  float* act;          // [k + S][F]
+  float* y_shared;     // [H]
+  uint16_t* xn;        // [H] normalised input (stack)
+  unsigned* ticket;    // router completion counter
+  // optional user outputs
+  float* logits_out;
+  int32_t* idx_out;
+  float* w_out;
+};
+
+hipError_t launch_router_topk_t1(const LayerT1& L, bool with_shared, hipStream_t s);
+hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* idx,
+                            float* act, bool with_shared_down, hipStream_t s);
+hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s);
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,62 @@
+"""GPU parity of the 8-layer decode stack (RMSNorm -> MoE -> residual, bf16
+hidden state between layers) against the fp64 oracle.
+
+Teacher-forced: oracle layer l is fed the GPU's own bf16 h_l, so every layer
+is checked on identical inputs.  End to end: the oracle chain from h_0 is
+compared with the GPU chain; the activation draw (tests/golden/
+stack8_token.json, written by make_stack_token.py from the oracle alone) has
+a top-k gap of at least 1e-2 at every layer of the oracle chain.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from gpu_helpers import (TOL, G, M, O, check_topk, dev_u16, host_u16, max_err_ratio, pmap,
+                         release_device_layers, shape_of, torch, weights_of, workspace)
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_stack8_teacher_forced_and_end_to_end():
+    t = torch()
+    release_device_layers()
+    w = G.WORKLOADS["k3_stack8"]
+    with open(os.path.join(GOLDEN, "stack8_token.json")) as f:
+        draw = json.load(f)["draw"]
+    layers = [G.DeviceLayer(w, l) for l in range(w.L)]
+    x = G.token(w, draw)
+    hidden = dev_u16(x.reshape(1, -1))
+    trace = t.empty((w.L, 1, w.H), dtype=t.int16, device="cuda")
+    idx = t.empty((w.L, 1, w.k), dtype=t.int32, device="cuda")
+    ws = workspace(w, 1)
+    M.decode_stack(shape_of(w), [weights_of(dl) for dl in layers], [dl.gamma for dl in layers],
+                   w.eps, hidden, 1, idx, trace, ws)
+    t.cuda.synchronize()
+    tr = host_u16(trace)
+    gi = idx.cpu().numpy()
+    assert np.array_equal(host_u16(hidden)[0], tr[-1, 0])
+    ol = []
+    for l, dl in enumerate(layers):
+        hx = G.HostExperts(w, l)
+        ol.append(dict(router=dl.router_host, gamma=dl.gamma_host, k=w.k, routed=hx.routed,
+                       shared=hx.shared()))
+    # teacher forced: layer l on the GPU's h_l
+    teacher = [x.reshape(1, -1)] + [tr[l] for l in range(w.L - 1)]
+    recs = O.moe_stack(x, ol, w.eps, teacher=teacher, pmap=pmap)
+    for l, r in enumerate(recs):
+        n = check_topk(gi[l], r, w.k)
+        err = max_err_ratio(tr[l], r["out"])[0]
+        print(f"layer {l}: topk checked={n} max_err/rms={err:.3e}")
+        assert err <= TOL, (l, err)
+    # end to end: the oracle's own chain
+    chain = O.moe_stack(x, ol, w.eps, pmap=pmap)
+    for l, r in enumerate(chain):
+        assert check_topk(gi[l], r, w.k, gap=1e-2) == 1, l
+    err = max_err_ratio(tr[-1], chain[-1]["out"])[0]
+    print(f"end to end: max_err/rms={err:.3e}")
+    assert err <= TOL
+    del layers
+    release_device_layers()
