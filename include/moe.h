@@ -31,11 +31,11 @@
  *    codes must be 16-byte aligned.  The reduction dimension is the row:
  *    C = H for gate/up, C = F for down.
  *  - Workspace: `ws` is a 16-byte aligned device buffer of at least
- *    moe_workspace_size() bytes.  Its first MOE_WS_COUNTER_BYTES bytes hold
- *    completion counters that must be zero before the first call
- *    (moe_workspace_init() zero-fills the whole buffer); every call leaves
- *    them at zero again, so one workspace serves any number of calls.  The
- *    rest is scratch that each call writes before it reads it.  Calls that
+ *    moe_workspace_size() bytes.  Its first MOE_WS_COUNTER_BYTES bytes are
+ *    reserved for counters and must be zero before the first call
+ *    (moe_workspace_init() zero-fills the whole buffer); calls leave them at
+ *    zero.  The rest is scratch that each call writes before it reads it, so
+ *    one workspace serves any number of calls on one stream.  Calls that
  *    overlap in time (different streams) need different workspaces.
  *  - Expert indices read from device memory (topk_idx arguments, or the
  *    router's own output) are clamped to [0, E) before addressing weights;

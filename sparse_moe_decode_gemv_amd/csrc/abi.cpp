@@ -17,7 +17,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t ticket, logits, idx, wts, act, y_shared, xn, group, total;
+  size_t reserved, logits, idx, wts, act, y_shared, xn, group, total;
 };
 
 WsLayout ws_layout(const moe_shape& s, int T) {
@@ -29,7 +29,7 @@ WsLayout ws_layout(const moe_shape& s, int T) {
     return at;
   };
   const size_t nslot = (size_t)s.top_k + (size_t)s.n_shared;
-  L.ticket = take(kAlign);
+  L.reserved = take(kAlign);
   L.logits = take(sizeof(float) * (size_t)T * s.n_experts);
   L.idx = take(sizeof(int32_t) * (size_t)T * s.top_k);
   L.wts = take(sizeof(float) * (size_t)T * s.top_k);
@@ -120,7 +120,6 @@ LayerT1 make_layer(const moe_shape* s, const moe_layer_weights* w, void* ws) {
       L.sd_scales = w->s_down.scales;
     }
   }
-  L.ticket = (unsigned*)(b + W.ticket);
   L.logits = (float*)(b + W.logits);
   L.idx = (int32_t*)(b + W.idx);
   L.wts = (float*)(b + W.wts);
@@ -130,12 +129,14 @@ LayerT1 make_layer(const moe_shape* s, const moe_layer_weights* w, void* ws) {
   return L;
 }
 
-// One full single-token layer: K1, K2, K3 on one stream.
+// One full single-token layer: K1a, K1b, K2, K3 on one stream.
 int run_layer_t1(LayerT1& L, hipStream_t st) {
-  hipError_t e = moe::launch_router_topk_t1(L, true, st);
+  hipError_t e = moe::launch_router_t1(L, true, st);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_topk_t1(L, true, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const uint16_t* xin = L.gamma ? L.xn : L.x;
-  e = moe::launch_gateup_t1(L, xin, L.idx, L.act, true, st);
+  e = moe::launch_gateup_t1(L, xin, L.idx, L.act, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_down_combine_t1(L, st));
 }
@@ -184,7 +185,8 @@ int moe_router_topk(const moe_shape* shape, const uint16_t* x, const uint16_t* r
   L.idx_out = topk_idx;
   L.w_out = topk_w;
   L.logits_out = logits;
-  return hip_status(moe::launch_router_topk_t1(L, false, (hipStream_t)stream));
+  if (moe::launch_router_t1(L, false, (hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_topk_t1(L, false, (hipStream_t)stream));
 }
 
 int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
@@ -198,7 +200,7 @@ int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const 
   if ((rc = check_ws(shape, n_tokens, ws, ws_bytes))) return rc;
   if (n_tokens > 1) return MOE_ERR_UNSUPPORTED;
   LayerT1 L = make_layer(shape, w, ws);
-  return hip_status(moe::launch_gateup_t1(L, x, topk_idx, act, false, (hipStream_t)stream));
+  return hip_status(moe::launch_gateup_t1(L, x, topk_idx, act, (hipStream_t)stream));
 }
 
 int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,

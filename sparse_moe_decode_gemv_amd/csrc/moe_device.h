@@ -14,8 +14,20 @@ namespace moe {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kWave = 64;
+
+// Streaming loads of static weights: each weight byte is read once per call,
+// so the loads carry the nontemporal hint and do not displace cached
+// activations.
+__device__ __forceinline__ uint4 ld_stream16(const uint8_t* p) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint32_t ld_stream8(const uint8_t* p) {
+  return __builtin_nontemporal_load(p);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
@@ -82,10 +94,43 @@ __device__ __forceinline__ float block_dot_f32(const uint4 c, const float* av) {
   return a0 + a1;
 }
 
+// Sum over aligned groups of `width` lanes (width a power of two, 4..64) by
+// DPP: butterflies inside quads, half rows and rows of 16 lanes, then row
+// broadcasts across rows.  The group's total is valid in the group's last
+// lane (lane % width == width - 1); other lanes hold partial sums.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_term(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float group_sum_last(float v, int width) {
+  v += dpp_term<0xB1, 0xF>(v);                  // quad_perm 1,0,3,2
+  v += dpp_term<0x4E, 0xF>(v);                  // quad_perm 2,3,0,1
+  if (width >= 8) v += dpp_term<0x141, 0xF>(v);   // row_half_mirror
+  if (width >= 16) v += dpp_term<0x140, 0xF>(v);  // row_mirror
+  if (width >= 32) v += dpp_term<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  if (width >= 64) v += dpp_term<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).
 __device__ __forceinline__ float group_sum(float v, int width) {
   for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
+}
+
+// Maximum over the 64 lanes, returned uniformly: DPP butterflies inside each
+// row of 16 lanes, then the four row results are read out and combined.
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false)); // row_half_mirror
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false)); // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return umax32(umax32(r0, r1), umax32(r2, r3));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -107,14 +152,6 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
 __device__ __forceinline__ float f32_from_order_key(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
   return __uint_as_float(u);
-}
-
-// Agent-scope release/acquire fences (all XCDs of the device).
-__device__ __forceinline__ void fence_release_agent() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-}
-__device__ __forceinline__ void fence_acquire_agent() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 }  // namespace moe

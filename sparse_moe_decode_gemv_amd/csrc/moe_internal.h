@@ -53,19 +53,21 @@ struct LayerT1 {
   float* logits;       // [E]
   int32_t* idx;        // [k]
   float* wts;          // [k]
-  float* act;          // [k + S][F]
-  float* y_shared;     // [H]
+  float* act;          // [k + S][F]: routed slots, then the shared expert
+  float* y_shared;     // [H] shared expert output
   uint16_t* xn;        // [H] normalised input (stack)
-  unsigned* ticket;    // router completion counter
   // optional user outputs
   float* logits_out;
   int32_t* idx_out;
   float* w_out;
 };
 
-hipError_t launch_router_topk_t1(const LayerT1& L, bool with_shared, hipStream_t s);
+// K1a router (+ shared gate/up), K1b top-k (+ shared down), K2 gate/up,
+// K3 down + combine; with_shared = false skips the shared-expert work.
+hipError_t launch_router_t1(const LayerT1& L, bool with_shared, hipStream_t s);
+hipError_t launch_topk_t1(const LayerT1& L, bool with_shared, hipStream_t s);
 hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* idx,
-                            float* act, bool with_shared_down, hipStream_t s);
+                            float* act, hipStream_t s);
 hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s);
 
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);

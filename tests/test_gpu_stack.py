@@ -2,10 +2,16 @@
 hidden state between layers) against the fp64 oracle.
 
 Teacher-forced: oracle layer l is fed the GPU's own bf16 h_l, so every layer
-is checked on identical inputs.  End to end: the oracle chain from h_0 is
-compared with the GPU chain; the activation draw (tests/golden/
-stack8_token.json, written by make_stack_token.py from the oracle alone) has
-a top-k gap of at least 1e-2 at every layer of the oracle chain.
+is checked on identical inputs against the per-layer bar (max-abs-error <=
+2e-2 * rms) and, element by element, against the correctly rounded oracle
+value.  End to end: the oracle chain from h_0 is compared with the GPU chain;
+the activation draw (tests/golden/stack8_token.json, written by
+make_stack_token.py from the oracle alone) has a top-k gap of at least 1e-2
+at every layer of the oracle chain, so the selected sets must agree at every
+layer.  The two bf16 chains drift apart by rounding alone (one ulp flipped in
+1% of one layer's outputs moves the oracle's own chain by ~4e-2 * rms after
+seven more layers), so the final output is held to the per-layer bar summed
+over the layers, L * 2e-2 * rms.
 """
 import json
 import os
@@ -18,6 +24,25 @@ from gpu_helpers import (TOL, G, M, O, check_topk, dev_u16, host_u16, max_err_ra
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+# Share of a layer's bf16 outputs allowed to differ from the oracle's fp64
+# output rounded to nearest even: fp32 accumulation leaves the pre-rounding
+# value within ~1e-5 of the summands' scale, so only values that close to a
+# rounding boundary round the other way (by one ulp, or by a few ulps where
+# the residual and the MoE output cancel and the result is small).
+MAX_FLIPS = 0.02
+
+
+def _order(b):
+    b = b.astype(np.int64)
+    return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)
+
+
+def bf16_mismatch(gpu_bits, ref_out):
+    """(share of elements where the GPU's bf16 differs from the correctly
+    rounded oracle value, largest distance in ulps)."""
+    want = O.f64_to_bf16(ref_out)
+    d = np.abs(_order(np.asarray(gpu_bits, np.uint16)) - _order(want))
+    return float((d != 0).mean()), int(d.max())
 
 
 def test_stack8_teacher_forced_and_end_to_end():
@@ -49,14 +74,20 @@ def test_stack8_teacher_forced_and_end_to_end():
     for l, r in enumerate(recs):
         n = check_topk(gi[l], r, w.k)
         err = max_err_ratio(tr[l], r["out"])[0]
-        print(f"layer {l}: topk checked={n} max_err/rms={err:.3e}")
+        flips, worst = bf16_mismatch(tr[l][0], r["out"][0])
+        print(f"layer {l}: topk checked={n} max_err/rms={err:.3e} "
+              f"bf16 != rounded oracle: {flips:.4f} of elements, max {worst} ulp")
         assert err <= TOL, (l, err)
-    # end to end: the oracle's own chain
+        assert flips <= MAX_FLIPS, (l, flips, worst)
+    # end to end: the oracle's own chain.  Its hidden states drift from the
+    # GPU's by bf16 ulps layer after layer, so only the selected sets (k-th to
+    # (k+1)-th gap >= 1e-2 at every layer for this draw) are compared; the
+    # order within a set is checked above, where both sides share the input.
     chain = O.moe_stack(x, ol, w.eps, pmap=pmap)
     for l, r in enumerate(chain):
-        assert check_topk(gi[l], r, w.k, gap=1e-2) == 1, l
+        assert check_topk(gi[l], r, w.k, ordered=False, gap=1e-2) == 1, l
     err = max_err_ratio(tr[-1], chain[-1]["out"])[0]
-    print(f"end to end: max_err/rms={err:.3e}")
-    assert err <= TOL
+    print(f"end to end: max_err/rms={err:.3e} (bound {w.L * TOL:.2f})")
+    assert err <= w.L * TOL
     del layers
     release_device_layers()
