@@ -133,6 +133,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return umax32(umax32(r0, r1), umax32(r2, r3));
 }
 
+// Inclusive prefix sum over the 64 lanes (DPP row shifts, then row
+// broadcasts across rows).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_term_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp_term_u32<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_term_u32<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_term_u32<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_term_u32<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_term_u32<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_term_u32<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
