@@ -54,13 +54,16 @@ def mx_bytes(rows: int, cols: int) -> int:
     return rows * cols // 2 + rows * cols // 32
 
 
-def layer_bytes(w) -> int:
-    """Compulsory HBM bytes of one decode layer per token: x in, out, router
-    rows, and the touched experts (k routed + S shared; residual == x)."""
+def layer_bytes(w, touched=None) -> int:
+    """Compulsory HBM bytes of one decode layer: x in, out, router rows, and
+    every touched expert once (the k routed experts of each token; at batch
+    T > 1 the distinct experts the batch selected) plus the shared expert;
+    the residual is x."""
     expert = 2 * mx_bytes(w.F, w.H) + mx_bytes(w.H, w.F)
     shared = w.S * (2 * mx_bytes(w.Fs, w.H) + mx_bytes(w.H, w.Fs))
     gamma = 2 * w.H if w.L > 1 else 0
-    return w.T * (2 * w.H + 2 * w.H) + 2 * w.E * w.H + w.T * w.k * expert + shared + gamma
+    n = w.T * w.k if touched is None else touched
+    return w.T * (2 * w.H + 2 * w.H) + 2 * w.E * w.H + n * expert + shared + gamma
 
 
 def gateup_bytes(w) -> int:
@@ -141,7 +144,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="k3_batch1",
-                    choices=["tiny", "k3_batch1", "k3_tp16_slice", "k3_stack8"])
+                    choices=["tiny", "k3_batch1", "k3_tp16_slice", "k3_stack8",
+                             "k3_batch64_zipf"])
     ap.add_argument("--sets", type=int, default=4, help="resident weight sets rotated")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly (no graph), e.g. under counter profiling")
@@ -188,21 +192,36 @@ def main():
     shape = M.make_shape(w.H, w.E, w.k, w.F, w.S, w.Fs)
     wts = [[M.make_weights(d.router, d.gate, d.up, d.down, d.s_gate, d.s_up, d.s_down)
             for d in s] for s in sets]
-    toks_host = [G.token(w, d) for d in range(ROT_TOKENS)]
-    xs = torch.from_numpy(np.stack(toks_host).view(np.int16)).cuda()
+    T = w.T
+    toks_host = [np.stack([G.token(w, ROT_TOKENS * b + d) for d in range(T)])
+                 for b in range(ROT_TOKENS)]           # ROT_TOKENS batches of T tokens
+    xs = torch.from_numpy(np.stack(toks_host).view(np.int16)).cuda()   # [R][T][H]
     outs = torch.empty_like(xs)
     hid = xs.clone()
-    ws = torch.empty(M.workspace_size(shape, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(M.workspace_size(shape, T), dtype=torch.uint8, device="cuda")
     M.workspace_init(ws)
 
     def step(i):
         s, t = i % nsets, i % ROT_TOKENS
         if stack:
-            M.decode_stack(shape, wts[s], [d.gamma for d in sets[s]], w.eps, hid[t:t + 1], 1,
+            M.decode_stack(shape, wts[s], [d.gamma for d in sets[s]], w.eps, hid[t], T,
                            None, None, ws)
         else:
-            M.decode_layer(shape, wts[s][0], xs[t:t + 1], xs[t:t + 1], outs[t:t + 1], 1, None,
-                           None, ws)
+            M.decode_layer(shape, wts[s][0], xs[t], xs[t], outs[t], T, None, None, ws)
+
+    touched = None
+    if T > 1 and not stack:
+        # distinct experts each (weight set, batch) selects, for the byte count
+        idx = torch.empty((T, w.k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((T, w.k), dtype=torch.float32, device="cuda")
+        counts = []
+        for i in range(ROT_TOKENS):
+            s_, t_ = i % nsets, i % ROT_TOKENS
+            M.router_topk(shape, xs[t_], sets[s_][0].router, T, idx, tw, None, ws)
+            counts.append(len(np.unique(idx.cpu().numpy())))
+        touched = float(np.mean(counts))
+        log(f"[bench] distinct experts per batch: mean {touched:.1f}, "
+            f"min {min(counts)}, max {max(counts)}")
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
@@ -249,7 +268,7 @@ def main():
 
     ms_per_step = total_ms / K
     us_layer = ms_per_step * 1e3 / nlayers
-    lb = layer_bytes(w)
+    lb = int(layer_bytes(w, touched))
     layer_gbps = lb / (us_layer * 1e-6) / 1e9
     log(f"[bench] {K} steps in {total_ms:.3f} ms: {us_layer:.2f} µs/layer, "
         f"{layer_gbps:.0f} GB/s algorithmic ({lb} B/layer), "
@@ -260,19 +279,19 @@ def main():
 
     # ---- dominant kernel alone: routed gate/up over the same rotation
     roofline = None
-    if not stack:
+    if not stack and T == 1:
         k = w.k
         idx = torch.empty((nsets, ROT_TOKENS, k), dtype=torch.int32, device="cuda")
         tw = torch.empty((nsets, ROT_TOKENS, k), dtype=torch.float32, device="cuda")
         for s in range(nsets):
             for t in range(ROT_TOKENS):
-                M.router_topk(shape, xs[t:t + 1], sets[s][0].router, 1, idx[s, t:t + 1],
+                M.router_topk(shape, xs[t], sets[s][0].router, 1, idx[s, t:t + 1],
                               tw[s, t:t + 1], None, ws)
         act = torch.empty((k, w.F), dtype=torch.float32, device="cuda")
 
         def gu(i):
             s, t = i % nsets, i % ROT_TOKENS
-            M.expert_gateup(shape, wts[s][0], xs[t:t + 1], idx[s, t:t + 1], 1, act, ws)
+            M.expert_gateup(shape, wts[s][0], xs[t], idx[s, t:t + 1], 1, act, ws)
 
         for i in range(ROT_TOKENS):
             gu(i)
@@ -310,7 +329,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host ...")
-        cpu = cpu_baseline(w, [d.router_host for d in sets[0]], toks_host[:8], args.cpu_seconds)
+        cpu = cpu_baseline(w, [d.router_host for d in sets[0]],
+                           [b[0] for b in toks_host[:8]], args.cpu_seconds)
         log(f"[bench] oracle: {cpu['value']} µs/layer on {cpu['cores']} threads")
 
     line = {
@@ -322,7 +342,7 @@ def main():
                                f"shared={w.S}x{w.Fs} layers={nlayers}",
                    "global_batch": w.T, "weight_sets": nsets,
                    "timing": "eager" if args.eager else "hipGraph of 16 steps"},
-        "layer_tokens_per_s": round(1e6 / us_layer, 1),
+        "layer_tokens_per_s": round(T * 1e6 / us_layer, 1),
         "layer_hbm": {"bytes": lb, "achieved": round(layer_gbps, 1), "unit": "GB/s",
                       "frac": round(layer_gbps / PEAK_HBM_GBPS, 4)},
         "roofline": roofline,

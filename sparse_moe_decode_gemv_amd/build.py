@@ -19,7 +19,7 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang",
              "-packed-fp32-ops", "-ffp-contract=fast"]
 
-DECODE_SOURCES = ["abi.cpp", "moe_t1.hip"]
+DECODE_SOURCES = ["abi.cpp", "moe_t1.hip", "moe_batched.hip"]
 LIB_DECODE = os.path.join(HERE, "libmoe_decode.so")
 LIB_INPUTS = os.path.join(ROOT, "moe_inputs", "libmoe_inputs.so")
 

@@ -5,41 +5,88 @@
 
 #include <hip/hip_runtime.h>
 
-#include <numeric>
-
 #include "moe_internal.h"
 
 namespace {
 
 using moe::LayerT1;
+using moe::LayerTB;
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-struct WsLayout {
-  size_t reserved, logits, idx, wts, act, y_shared, xn, group, total;
-};
-
-WsLayout ws_layout(const moe_shape& s, int T) {
-  WsLayout L{};
+// Bump allocator over the workspace (offsets only).
+struct Carver {
   size_t o = 0;
-  auto take = [&](size_t bytes) {
+  size_t take(size_t bytes) {
     const size_t at = o;
     o += align_up(bytes);
     return at;
-  };
+  }
+};
+
+// Single-token layout.
+struct WsT1 {
+  size_t reserved, logits, idx, wts, act, y_shared, xn, total;
+};
+
+WsT1 ws_t1(const moe_shape& s) {
+  WsT1 L{};
+  Carver c;
   const size_t nslot = (size_t)s.top_k + (size_t)s.n_shared;
-  L.reserved = take(kAlign);
-  L.logits = take(sizeof(float) * (size_t)T * s.n_experts);
-  L.idx = take(sizeof(int32_t) * (size_t)T * s.top_k);
-  L.wts = take(sizeof(float) * (size_t)T * s.top_k);
-  L.act = take(sizeof(float) * (size_t)T * nslot * s.ffn);
-  L.y_shared = take(sizeof(float) * (size_t)T * s.hidden);
-  L.xn = take(sizeof(uint16_t) * (size_t)T * s.hidden);
-  L.group = take(sizeof(int32_t) * (size_t)(s.n_experts + 1 + T * s.top_k));
-  L.total = o;
+  L.reserved = c.take(MOE_WS_COUNTER_BYTES);
+  L.logits = c.take(sizeof(float) * s.n_experts);
+  L.idx = c.take(sizeof(int32_t) * s.top_k);
+  L.wts = c.take(sizeof(float) * s.top_k);
+  L.act = c.take(sizeof(float) * nslot * s.ffn);
+  L.y_shared = c.take(sizeof(float) * s.hidden);
+  L.xn = c.take(sizeof(uint16_t) * s.hidden);
+  L.total = c.o;
   return L;
 }
+
+// Grouping part of the batched layout (also used by moe_group_by_expert).
+struct WsGroup {
+  size_t ginfo, g_expert, g_start, g_count, order, pos_of;
+};
+
+WsGroup ws_group(Carver& c, int E, int T, int k) {
+  WsGroup G{};
+  const size_t P = (size_t)T * k;
+  G.ginfo = c.take(4 * sizeof(int32_t));
+  G.g_expert = c.take(sizeof(int32_t) * (E + 1));
+  G.g_start = c.take(sizeof(int32_t) * (E + 1));
+  G.g_count = c.take(sizeof(int32_t) * (E + 1));
+  G.order = c.take(sizeof(int32_t) * (P + T));
+  G.pos_of = c.take(sizeof(int32_t) * P);
+  return G;
+}
+
+// Batched (T >= 2) layout.
+struct WsTB {
+  size_t reserved, part, idx, wts, act_hi, act_lo, y, xn, total;
+  WsGroup grp;
+};
+
+WsTB ws_tb(const moe_shape& s, int T) {
+  WsTB L{};
+  Carver c;
+  const size_t P = (size_t)T * s.top_k;
+  const size_t npos = P + (size_t)s.n_shared * T;
+  L.reserved = c.take(MOE_WS_COUNTER_BYTES);
+  L.part = c.take(sizeof(float) * moe::router_splits(s.hidden) * T * s.n_experts);
+  L.idx = c.take(sizeof(int32_t) * P);
+  L.wts = c.take(sizeof(float) * P);
+  L.grp = ws_group(c, s.n_experts, T, s.top_k);
+  L.act_hi = c.take(sizeof(uint16_t) * npos * s.ffn);
+  L.act_lo = c.take(sizeof(uint16_t) * npos * s.ffn);
+  L.y = c.take(sizeof(float) * npos * s.hidden);
+  L.xn = c.take(sizeof(uint16_t) * (size_t)T * s.hidden);
+  L.total = c.o;
+  return L;
+}
+
+size_t ws_needed(const moe_shape& s, int T) { return T <= 1 ? ws_t1(s).total : ws_tb(s, T).total; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -67,7 +114,7 @@ int check_tokens(int32_t T) {
 
 int check_ws(const moe_shape* s, int32_t T, const void* ws, size_t ws_bytes) {
   if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
-  if (ws_layout(*s, T).total > ws_bytes) return MOE_ERR_WORKSPACE;
+  if (ws_needed(*s, T) > ws_bytes) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 
@@ -94,8 +141,28 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+template <class Layer>
+void set_weights(Layer& L, const moe_shape* s, const moe_layer_weights* w) {
+  if (!w) return;
+  L.router_w = w->router_w;
+  L.g_codes = w->gate.codes;
+  L.g_scales = w->gate.scales;
+  L.u_codes = w->up.codes;
+  L.u_scales = w->up.scales;
+  L.d_codes = w->down.codes;
+  L.d_scales = w->down.scales;
+  if (s->n_shared) {
+    L.sg_codes = w->s_gate.codes;
+    L.sg_scales = w->s_gate.scales;
+    L.su_codes = w->s_up.codes;
+    L.su_scales = w->s_up.scales;
+    L.sd_codes = w->s_down.codes;
+    L.sd_scales = w->s_down.scales;
+  }
+}
+
 LayerT1 make_layer(const moe_shape* s, const moe_layer_weights* w, void* ws) {
-  const WsLayout W = ws_layout(*s, 1);
+  const WsT1 W = ws_t1(*s);
   char* b = (char*)ws;
   LayerT1 L{};
   L.H = s->hidden;
@@ -103,23 +170,7 @@ LayerT1 make_layer(const moe_shape* s, const moe_layer_weights* w, void* ws) {
   L.k = s->top_k;
   L.F = s->ffn;
   L.S = s->n_shared;
-  if (w) {
-    L.router_w = w->router_w;
-    L.g_codes = w->gate.codes;
-    L.g_scales = w->gate.scales;
-    L.u_codes = w->up.codes;
-    L.u_scales = w->up.scales;
-    L.d_codes = w->down.codes;
-    L.d_scales = w->down.scales;
-    if (s->n_shared) {
-      L.sg_codes = w->s_gate.codes;
-      L.sg_scales = w->s_gate.scales;
-      L.su_codes = w->s_up.codes;
-      L.su_scales = w->s_up.scales;
-      L.sd_codes = w->s_down.codes;
-      L.sd_scales = w->s_down.scales;
-    }
-  }
+  set_weights(L, s, w);
   L.logits = (float*)(b + W.logits);
   L.idx = (int32_t*)(b + W.idx);
   L.wts = (float*)(b + W.wts);
@@ -128,6 +179,39 @@ LayerT1 make_layer(const moe_shape* s, const moe_layer_weights* w, void* ws) {
   L.xn = (uint16_t*)(b + W.xn);
   return L;
 }
+
+void set_group(LayerTB& L, const WsGroup& G, char* b) {
+  L.ginfo = (int32_t*)(b + G.ginfo);
+  L.g_expert = (int32_t*)(b + G.g_expert);
+  L.g_start = (int32_t*)(b + G.g_start);
+  L.g_count = (int32_t*)(b + G.g_count);
+  L.order = (int32_t*)(b + G.order);
+  L.pos_of = (int32_t*)(b + G.pos_of);
+}
+
+LayerTB make_layer_tb(const moe_shape* s, const moe_layer_weights* w, void* ws, int T) {
+  const WsTB W = ws_tb(*s, T);
+  char* b = (char*)ws;
+  LayerTB L{};
+  L.T = T;
+  L.H = s->hidden;
+  L.E = s->n_experts;
+  L.k = s->top_k;
+  L.F = s->ffn;
+  L.S = s->n_shared;
+  L.KS = moe::router_splits(s->hidden);
+  set_weights(L, s, w);
+  L.part = (float*)(b + W.part);
+  L.idx = (int32_t*)(b + W.idx);
+  L.wts = (float*)(b + W.wts);
+  set_group(L, W.grp, b);
+  L.act_hi = (uint16_t*)(b + W.act_hi);
+  L.act_lo = (uint16_t*)(b + W.act_lo);
+  L.y = (float*)(b + W.y);
+  return L;
+}
+
+uint16_t* xn_tb(const moe_shape* s, void* ws, int T) { return (uint16_t*)((char*)ws + ws_tb(*s, T).xn); }
 
 // One full single-token layer: K1a, K1b, K2, K3 on one stream.
 int run_layer_t1(LayerT1& L, hipStream_t st) {
@@ -139,6 +223,16 @@ int run_layer_t1(LayerT1& L, hipStream_t st) {
   e = moe::launch_gateup_t1(L, xin, L.idx, L.act, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_down_combine_t1(L, st));
+}
+
+// One batched layer: router, top-k, grouping, gate/up, down, combine.
+int run_layer_tb(LayerTB& L, hipStream_t st) {
+  if (moe::launch_router_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_topk_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_group_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_gateup_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_down_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_combine_tb(L, st));
 }
 
 }  // namespace
@@ -160,7 +254,12 @@ int moe_workspace_size(const moe_shape* shape, int32_t max_tokens, size_t* bytes
   int rc;
   if ((rc = check_shape(shape)) || (rc = check_tokens(max_tokens))) return rc;
   if (!bytes) return MOE_ERR_INVALID_ARG;
-  *bytes = ws_layout(*shape, max_tokens < 1 ? 1 : max_tokens).total;
+  size_t n = ws_t1(*shape).total;
+  if (max_tokens >= 2) {
+    const size_t m = ws_tb(*shape, max_tokens).total;
+    n = m > n ? m : n;
+  }
+  *bytes = n;
   return MOE_OK;
 }
 
@@ -178,15 +277,25 @@ int moe_router_topk(const moe_shape* shape, const uint16_t* x, const uint16_t* r
   if (!x || !aligned16(x) || !router_w || !aligned16(router_w) || !topk_idx || !topk_w)
     return MOE_ERR_INVALID_ARG;
   if ((rc = check_ws(shape, n_tokens, ws, ws_bytes))) return rc;
-  if (n_tokens > 1) return MOE_ERR_UNSUPPORTED;
-  LayerT1 L = make_layer(shape, nullptr, ws);
+  const hipStream_t st = (hipStream_t)stream;
+  if (n_tokens == 1) {
+    LayerT1 L = make_layer(shape, nullptr, ws);
+    L.router_w = router_w;
+    L.x = x;
+    L.idx_out = topk_idx;
+    L.w_out = topk_w;
+    L.logits_out = logits;
+    if (moe::launch_router_t1(L, false, st) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(moe::launch_topk_t1(L, false, st));
+  }
+  LayerTB L = make_layer_tb(shape, nullptr, ws, n_tokens);
   L.router_w = router_w;
   L.x = x;
   L.idx_out = topk_idx;
   L.w_out = topk_w;
   L.logits_out = logits;
-  if (moe::launch_router_t1(L, false, (hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_topk_t1(L, false, (hipStream_t)stream));
+  if (moe::launch_router_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_topk_tb(L, st));
 }
 
 int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
@@ -211,20 +320,30 @@ int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const u
   if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
   if (n_tokens == 0) return MOE_OK;
   if ((rc = check_weights(shape, w, true))) return rc;
-  if (!x || !aligned16(x) || !out) return MOE_ERR_INVALID_ARG;
+  if (!x || !aligned16(x) || !out || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  if (residual && !aligned16(residual)) return MOE_ERR_INVALID_ARG;
   const size_t vec = sizeof(uint16_t) * (size_t)n_tokens * shape->hidden;
   if (residual != x && overlaps(out, vec, x, vec)) return MOE_ERR_INVALID_ARG;
   if (residual && residual != out && overlaps(out, vec, residual, vec)) return MOE_ERR_INVALID_ARG;
   if ((rc = check_ws(shape, n_tokens, ws, ws_bytes))) return rc;
   if (overlaps(ws, ws_bytes, out, vec) || overlaps(ws, ws_bytes, x, vec)) return MOE_ERR_INVALID_ARG;
-  if (n_tokens > 1) return MOE_ERR_UNSUPPORTED;
-  LayerT1 L = make_layer(shape, w, ws);
+  const hipStream_t st = (hipStream_t)stream;
+  if (n_tokens == 1) {
+    LayerT1 L = make_layer(shape, w, ws);
+    L.x = x;
+    L.residual = residual;
+    L.out = out;
+    L.idx_out = topk_idx_out;
+    L.w_out = topk_w_out;
+    return run_layer_t1(L, st);
+  }
+  LayerTB L = make_layer_tb(shape, w, ws, n_tokens);
   L.x = x;
   L.residual = residual;
   L.out = out;
   L.idx_out = topk_idx_out;
   L.w_out = topk_w_out;
-  return run_layer_t1(L, (hipStream_t)stream);
+  return run_layer_tb(L, st);
 }
 
 int moe_decode_stack(const moe_shape* shape, const moe_layer_weights* layers,
@@ -240,21 +359,37 @@ int moe_decode_stack(const moe_shape* shape, const moe_layer_weights* layers,
     if ((rc = check_weights(shape, &layers[l], true))) return rc;
     if (!gammas[l] || !aligned16(gammas[l])) return MOE_ERR_INVALID_ARG;
   }
+  if (hidden_trace && !aligned16(hidden_trace)) return MOE_ERR_INVALID_ARG;
   if ((rc = check_ws(shape, n_tokens, ws, ws_bytes))) return rc;
   const size_t vec = sizeof(uint16_t) * (size_t)n_tokens * shape->hidden;
   if (overlaps(ws, ws_bytes, hidden, vec)) return MOE_ERR_INVALID_ARG;
-  if (n_tokens > 1) return MOE_ERR_UNSUPPORTED;
   const hipStream_t st = (hipStream_t)stream;
   for (int l = 0; l < n_layers; ++l) {
-    LayerT1 L = make_layer(shape, &layers[l], ws);
-    L.x = hidden;
-    L.gamma = gammas[l];
-    L.eps = eps;
-    L.residual = hidden;
-    L.out = hidden;
-    L.trace = hidden_trace ? hidden_trace + (size_t)l * n_tokens * shape->hidden : nullptr;
-    L.idx_out = topk_idx_out ? topk_idx_out + (size_t)l * n_tokens * shape->top_k : nullptr;
-    if ((rc = run_layer_t1(L, st))) return rc;
+    uint16_t* trace = hidden_trace ? hidden_trace + (size_t)l * n_tokens * shape->hidden : nullptr;
+    int32_t* idx_out = topk_idx_out ? topk_idx_out + (size_t)l * n_tokens * shape->top_k : nullptr;
+    if (n_tokens == 1) {
+      LayerT1 L = make_layer(shape, &layers[l], ws);
+      L.x = hidden;
+      L.gamma = gammas[l];
+      L.eps = eps;
+      L.residual = hidden;
+      L.out = hidden;
+      L.trace = trace;
+      L.idx_out = idx_out;
+      if ((rc = run_layer_t1(L, st))) return rc;
+    } else {
+      uint16_t* xn = xn_tb(shape, ws, n_tokens);
+      if (moe::launch_rmsnorm_tb(hidden, gammas[l], eps, n_tokens, shape->hidden, xn, st) !=
+          hipSuccess)
+        return MOE_ERR_HIP;
+      LayerTB L = make_layer_tb(shape, &layers[l], ws, n_tokens);
+      L.x = xn;
+      L.residual = hidden;
+      L.out = hidden;
+      L.trace = trace;
+      L.idx_out = idx_out;
+      if ((rc = run_layer_tb(L, st))) return rc;
+    }
   }
   return MOE_OK;
 }
@@ -262,9 +397,26 @@ int moe_decode_stack(const moe_shape* shape, const moe_layer_weights* layers,
 int moe_group_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t top_k,
                         int32_t n_experts, int32_t* offsets, int32_t* pairs, void* ws,
                         size_t ws_bytes, void* stream) {
-  (void)topk_idx; (void)n_tokens; (void)top_k; (void)n_experts; (void)offsets; (void)pairs;
-  (void)ws; (void)ws_bytes; (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  int rc;
+  if ((rc = check_tokens(n_tokens))) return rc;
+  if (top_k <= 0 || n_experts <= 0 || top_k > n_experts) return MOE_ERR_INVALID_ARG;
+  if (top_k > moe::kMaxTopK || n_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return MOE_OK;
+  if (!topk_idx || !offsets || !pairs) return MOE_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  Carver c;
+  const WsGroup G = ws_group(c, n_experts, n_tokens, top_k);
+  if (c.o > ws_bytes) return MOE_ERR_WORKSPACE;
+  LayerTB L{};
+  L.T = n_tokens;
+  L.E = n_experts;
+  L.k = top_k;
+  L.S = 0;
+  L.idx = const_cast<int32_t*>(topk_idx);
+  set_group(L, G, (char*)ws);
+  L.offsets_out = offsets;
+  L.pairs_out = pairs;
+  return hip_status(moe::launch_group_tb(L, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,556 @@
+// Batched decode layer (2 <= T <= 64 tokens): six kernels on one stream.
+//
+//  router   logits of all T tokens as bf16 MFMA tiles (16 experts x 16
+//           tokens per fragment), the reduction dimension split KS ways;
+//           partial sums go to the workspace.
+//  topk     one workgroup per token: adds the KS partials in a fixed order,
+//           then the radix top-k + softmax shared with the single-token path.
+//  group    one workgroup: a 64-bit token mask per expert gives each
+//           (token, slot) pair its stable rank inside its expert, hence a
+//           counting sort of the pairs by expert (pairs of an expert ordered
+//           by token), and the list of active experts; the shared expert is
+//           appended as one more group holding every token.
+//  gateup   grouped GEMM per (group, 16-row tile): A = 16 gate rows and 16 up
+//           rows, MXFP4 decoded to exact bf16 in registers; B = the group's
+//           token activations (bf16); fp32 accumulation; SiLU gating in the
+//           epilogue.  The gated activation a is stored as two bf16 parts,
+//           a_hi = bf16(a) and a_lo = bf16(a - a_hi), so that the down GEMM
+//           keeps ~16 significant bits of a on bf16 MFMA.
+//  down     grouped GEMM per (group, 16-row tile of the hidden size) over
+//           a_hi and a_lo -> fp32 expert outputs per sorted pair.
+//  combine  per token: residual + sum_j w_j y_j (slot order) + y_shared ->
+//           bf16; fixed order, no floating-point atomics.
+//
+// At batch 64 the selected experts are shared by several tokens (skewed
+// routing puts up to ~30 tokens on one expert, and the shared expert sees
+// all of them), so gate/up and down are real contractions and run on MFMA
+// (the pages' size-specialised kernels for larger batches: smzdm page,
+// section "四步改造"; the pages' fast path stops at 64 tokens: page "AI手搓
+// 1.2万行代码榨干GB300!…", section 03).  Weight bytes still dominate, so the
+// grouped kernels keep consecutive waves on consecutive row tiles of one
+// expert and stream the weights with nontemporal 16-byte loads.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 fragments (lane l = 16 q + r): A holds
+// A[r][8q .. 8q+7], B holds B[8q .. 8q+7][r], the result C[4q .. 4q+3][r].
+// The reduction index is permuted consistently in A and B: for a 128-wide
+// step, lane group q owns MXFP4 block q of the step (one 16-byte load) and
+// MFMA s of the step takes elements 8s .. 8s+7 of that block.
+#include "moe_device.h"
+#include "moe_internal.h"
+#include "moe_topk.h"
+
+namespace moe {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kBlk = 256;
+constexpr int kWv = kBlk / kWave;
+constexpr int kGroupBlock = 1024;
+constexpr int kTileRows = 16;
+constexpr int kMaxRouterSplits = 16;
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Eight MXFP4 elements (one code dword, element order) times the block scale,
+// as exact bf16 values.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  const bf16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int s) {
+  return s == 0 ? v.x : (s == 1 ? v.y : (s == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Inclusive scan over a workgroup of kGroupBlock threads (16 waves).
+__device__ __forceinline__ int block_incl_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int inc = (int)wave_incl_scan_u32((uint32_t)v);
+  if (lane == kWave - 1) wsum[wid] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wid; ++w) before += wsum[w];
+  __syncthreads();
+  return before + inc;
+}
+
+// ---------------------------------------------------------------- router
+// One wave per (16-expert tile, K split); KS splits of H, each a multiple of
+// 128, walked 128 elements (four MFMA steps) at a time with all loads of the
+// step issued first.  Tokens past T and experts past E read in-bounds
+// neighbours whose results are dropped.
+__global__ __launch_bounds__(kBlk) void kb_router(LayerTB L, int n_et) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+  const int w = blockIdx.x * kWv + wave_id();
+  const int et = w % n_et, ks = w / n_et;
+  if (ks >= L.KS) return;
+  const int Kc = L.H / L.KS;
+  const int k0 = ks * Kc;
+  const int NT = (L.T + 15) / 16;
+  const int erow = et * kTileRows + r < L.E ? et * kTileRows + r : L.E - 1;
+  const uint8_t* arow = reinterpret_cast<const uint8_t*>(L.router_w + (size_t)erow * L.H);
+  const uint8_t* brow[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int t = nt * 16 + r < L.T ? nt * 16 + r : L.T - 1;
+    brow[nt] = reinterpret_cast<const uint8_t*>(L.x + (size_t)t * L.H);
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = k0; kk < k0 + Kc; kk += 128) {
+    uint4 a[4], b[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = ld_stream16(arow + (size_t)(kk + 32 * s + 8 * q) * 2);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      if (nt < NT) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          b[nt][s] = *reinterpret_cast<const uint4*>(brow[nt] + (size_t)(kk + 32 * s + 8 * q) * 2);
+      }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      if (nt < NT) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[nt] = mfma(as_bf16x8(a[s]), as_bf16x8(b[nt][s]), acc[nt]);
+      }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int t = nt * 16 + r;
+    if (nt < NT && t < L.T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = et * kTileRows + 4 * q + i;
+        if (e < L.E) L.part[((size_t)ks * L.T + t) * L.E + e] = acc[nt][i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- top-k
+__global__ __launch_bounds__(kTopkBlock) void kb_topk(LayerTB L) {
+  __shared__ TopkLds tk;
+  const int t = blockIdx.x;
+  // all partial loads first (split index clamped, extra splits ignored), then
+  // the sums in split order
+  float v[kMaxRouterSplits][kTopkPerThread];
+#pragma unroll
+  for (int ks = 0; ks < kMaxRouterSplits; ++ks) {
+    const int kc = ks < L.KS ? ks : L.KS - 1;
+#pragma unroll
+    for (int i = 0; i < kTopkPerThread; ++i) {
+      const int e = threadIdx.x * kTopkPerThread + i;
+      v[ks][i] = L.part[((size_t)kc * L.T + t) * L.E + (e < L.E ? e : L.E - 1)];
+    }
+  }
+  float lg[kTopkPerThread];
+#pragma unroll
+  for (int i = 0; i < kTopkPerThread; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kMaxRouterSplits; ++ks) s += ks < L.KS ? v[ks][i] : 0.f;
+    lg[i] = s;
+    const int e = threadIdx.x * kTopkPerThread + i;
+    if (L.logits_out && e < L.E) L.logits_out[(size_t)t * L.E + e] = s;
+  }
+  const size_t o = (size_t)t * L.k;
+  topk_softmax_block(lg, L.E, L.k, tk, L.idx + o, L.wts + o, L.idx_out ? L.idx_out + o : nullptr,
+                     L.w_out ? L.w_out + o : nullptr);
+}
+
+// ---------------------------------------------------------------- group
+// Stable counting sort of the T k pairs by expert.  Each token's k experts
+// are distinct (top-k output), so the rank of pair (t, j) among the pairs of
+// expert e is the number of tokens below t that chose e: a popcount of the
+// expert's token mask.  (For caller-supplied indices that repeat an expert
+// within a token the grouping is unspecified, but every position stays in
+// bounds.)
+__global__ __launch_bounds__(kGroupBlock) void kb_group(LayerTB L) {
+  __shared__ uint32_t s_mask[kMaxExperts][2];
+  __shared__ int s_off[kMaxExperts];
+  __shared__ int s_wsum[kGroupBlock / kWave];
+  const int tid = threadIdx.x;
+  const int P = L.T * L.k;
+  s_mask[tid][0] = 0u;
+  s_mask[tid][1] = 0u;
+  __syncthreads();
+  for (int p = tid; p < P; p += kGroupBlock) {
+    int e = L.idx[p];
+    e = e < 0 ? 0 : (e >= L.E ? L.E - 1 : e);
+    const int t = p / L.k;
+    atomicOr(&s_mask[e][t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  const int cnt = tid < L.E ? __popc(s_mask[tid][0]) + __popc(s_mask[tid][1]) : 0;
+  const int act = cnt > 0 ? 1 : 0;
+  const int off_incl = block_incl_scan(cnt, s_wsum);
+  const int act_incl = block_incl_scan(act, s_wsum);
+  const int off = off_incl - cnt;
+  s_off[tid] = off;
+  if (act) {
+    const int a = act_incl - 1;
+    L.g_expert[a] = tid;
+    L.g_start[a] = off;
+    L.g_count[a] = cnt;
+  }
+  if (L.offsets_out && tid < L.E) L.offsets_out[tid] = off;
+  if (tid == kGroupBlock - 1) {
+    const int nact = act_incl;
+    L.ginfo[0] = nact + L.S;
+    if (L.S) {
+      L.g_expert[nact] = L.E;
+      L.g_start[nact] = P;
+      L.g_count[nact] = L.T;
+    }
+    if (L.offsets_out) L.offsets_out[L.E] = off_incl;
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += kGroupBlock) {
+    int e = L.idx[p];
+    e = e < 0 ? 0 : (e >= L.E ? L.E - 1 : e);
+    const int t = p / L.k;
+    const uint32_t m0 = s_mask[e][0], m1 = s_mask[e][1];
+    const int below = t < 32 ? __popc(m0 & ((1u << t) - 1u))
+                             : __popc(m0) + __popc(m1 & ((1u << (t - 32)) - 1u));
+    int pos = s_off[e] + below;
+    pos = pos < P ? pos : P - 1;
+    L.order[pos] = p;
+    L.pos_of[p] = pos;
+    if (L.pairs_out) L.pairs_out[pos] = p;
+  }
+  if (L.S)
+    for (int t = tid; t < L.T; t += kGroupBlock) L.order[P + t] = P + t;
+}
+
+// Token of a sorted pair id: routed pairs are t k + j, shared pairs P + t.
+__device__ __forceinline__ int token_of(const LayerTB& L, int pid) {
+  const int P = L.T * L.k;
+  int t = pid < P ? pid / L.k : pid - P;
+  return t < 0 ? 0 : (t >= L.T ? L.T - 1 : t);
+}
+
+// ---------------------------------------------------------------- gate/up
+// Items (group, 16-row tile) in group-major order; wave w takes items w,
+// w + nwaves, ... so that waves running together read consecutive row tiles
+// of one expert.  Per 128-wide step a lane loads one 16-byte code chunk (and
+// its scale) of a gate row and of an up row, and 64 bytes of its token's
+// activations; the next step's loads are issued before this step's MFMAs.
+struct GuStep {
+  uint4 ag, au, b[4];
+  uint32_t sg, su;
+};
+
+__device__ __forceinline__ void gu_load(GuStep& S, const uint8_t* gc, const uint8_t* gs,
+                                        const uint8_t* uc, const uint8_t* us, const uint8_t* xr,
+                                        int blk) {
+  S.ag = ld_stream16(gc + (size_t)blk * 16);
+  S.au = ld_stream16(uc + (size_t)blk * 16);
+  S.sg = ld_stream8(gs + blk);
+  S.su = ld_stream8(us + blk);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    S.b[s] = *reinterpret_cast<const uint4*>(xr + (size_t)(32 * blk + 8 * s) * 2);
+}
+
+__device__ __forceinline__ void gu_compute(const GuStep& S, f32x4& cg, f32x4& cu) {
+  const float fg = e8m0_to_f32(S.sg), fu = e8m0_to_f32(S.su);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8 bv = as_bf16x8(S.b[s]);
+    cg = mfma(fp4x8_to_bf16(dword_of(S.ag, s), fg), bv, cg);
+    cu = mfma(fp4x8_to_bf16(dword_of(S.au, s), fu), bv, cu);
+  }
+}
+
+__global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+  const int ng = L.ginfo[0];
+  const int tiles = L.F / kTileRows;
+  const int nitems = ng * tiles;
+  const int nblk = L.H / 32;  // MXFP4 blocks per gate/up row
+  const int nwaves = gridDim.x * kWv;
+  for (int it = blockIdx.x * kWv + wave_id(); it < nitems; it += nwaves) {
+    const int g = it / tiles, rt = it - g * tiles;
+    const int e = L.g_expert[g], start = L.g_start[g], m = L.g_count[g];
+    const bool sh = e >= L.E;
+    const size_t ebase = sh ? 0 : (size_t)e * L.F;
+    const int row = rt * kTileRows + r;
+    const size_t rsel = ebase + row;
+    const uint8_t* gc = (sh ? L.sg_codes : L.g_codes) + rsel * (L.H / 2);
+    const uint8_t* gs = (sh ? L.sg_scales : L.g_scales) + rsel * (L.H / 32);
+    const uint8_t* uc = (sh ? L.su_codes : L.u_codes) + rsel * (L.H / 2);
+    const uint8_t* us = (sh ? L.su_scales : L.u_scales) + rsel * (L.H / 32);
+    for (int n0 = 0; n0 < m; n0 += 16) {
+      const int c = n0 + r < m ? n0 + r : m - 1;
+      const int t = token_of(L, L.order[start + c]);
+      const uint8_t* xr = reinterpret_cast<const uint8_t*>(L.x + (size_t)t * L.H);
+      f32x4 cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
+      GuStep A, B;
+      gu_load(A, gc, gs, uc, us, xr, q);
+      for (int kb = 0; kb < nblk; kb += 8) {
+        if (kb + 4 < nblk) gu_load(B, gc, gs, uc, us, xr, kb + 4 + q);
+        gu_compute(A, cg, cu);
+        if (kb + 4 >= nblk) break;
+        if (kb + 8 < nblk) gu_load(A, gc, gs, uc, us, xr, kb + 8 + q);
+        gu_compute(B, cg, cu);
+      }
+      if (n0 + r < m) {
+        const size_t o = (size_t)(start + n0 + r) * L.F + rt * kTileRows + 4 * q;
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = silu(cg[i]) * cu[i];
+          hi[i] = f32_to_bf16(a);
+          lo[i] = f32_to_bf16(a - bf16_to_f32(hi[i]));
+        }
+        uint2 vh, vl;
+        vh.x = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
+        vh.y = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+        vl.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+        vl.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+        *reinterpret_cast<uint2*>(L.act_hi + o) = vh;
+        *reinterpret_cast<uint2*>(L.act_lo + o) = vl;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- down
+struct DnStep {
+  uint4 a, bh[4], bl[4];
+  uint32_t sc;
+};
+
+__device__ __forceinline__ void dn_load(DnStep& S, const uint8_t* dc, const uint8_t* ds,
+                                        const uint8_t* ah, const uint8_t* al, int blk) {
+  S.a = ld_stream16(dc + (size_t)blk * 16);
+  S.sc = ld_stream8(ds + blk);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    S.bh[s] = *reinterpret_cast<const uint4*>(ah + (size_t)(32 * blk + 8 * s) * 2);
+    S.bl[s] = *reinterpret_cast<const uint4*>(al + (size_t)(32 * blk + 8 * s) * 2);
+  }
+}
+
+__device__ __forceinline__ void dn_compute(const DnStep& S, f32x4& acc) {
+  const float f = e8m0_to_f32(S.sc);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8 av = fp4x8_to_bf16(dword_of(S.a, s), f);
+    acc = mfma(av, as_bf16x8(S.bh[s]), acc);
+    acc = mfma(av, as_bf16x8(S.bl[s]), acc);
+  }
+}
+
+__global__ __launch_bounds__(kBlk) void kb_down(LayerTB L) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+  const int ng = L.ginfo[0];
+  const int tiles = L.H / kTileRows;
+  const int nitems = ng * tiles;
+  const int nblk = L.F / 32;  // MXFP4 blocks per down row
+  const int nwaves = gridDim.x * kWv;
+  for (int it = blockIdx.x * kWv + wave_id(); it < nitems; it += nwaves) {
+    const int g = it / tiles, rt = it - g * tiles;
+    const int e = L.g_expert[g], start = L.g_start[g], m = L.g_count[g];
+    const bool sh = e >= L.E;
+    const size_t rsel = (sh ? 0 : (size_t)e * L.H) + rt * kTileRows + r;
+    const uint8_t* dc = (sh ? L.sd_codes : L.d_codes) + rsel * (L.F / 2);
+    const uint8_t* ds = (sh ? L.sd_scales : L.d_scales) + rsel * (L.F / 32);
+    for (int n0 = 0; n0 < m; n0 += 16) {
+      const int c = n0 + r < m ? n0 + r : m - 1;
+      const size_t ao = (size_t)(start + c) * L.F;
+      const uint8_t* ah = reinterpret_cast<const uint8_t*>(L.act_hi + ao);
+      const uint8_t* al = reinterpret_cast<const uint8_t*>(L.act_lo + ao);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      DnStep A, B;
+      dn_load(A, dc, ds, ah, al, q);
+      for (int kb = 0; kb < nblk; kb += 8) {
+        if (kb + 4 < nblk) dn_load(B, dc, ds, ah, al, kb + 4 + q);
+        dn_compute(A, acc);
+        if (kb + 4 >= nblk) break;
+        if (kb + 8 < nblk) dn_load(A, dc, ds, ah, al, kb + 8 + q);
+        dn_compute(B, acc);
+      }
+      if (n0 + r < m) {
+        float4 v;
+        v.x = acc[0];
+        v.y = acc[1];
+        v.z = acc[2];
+        v.w = acc[3];
+        *reinterpret_cast<float4*>(L.y + (size_t)(start + n0 + r) * L.H + rt * kTileRows + 4 * q) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+// Workgroup (token t, chunk of 8 kBlk hidden elements); each thread adds its
+// 8 elements over the slots in order, then the shared output and the
+// residual, and rounds once to bf16.
+__global__ __launch_bounds__(kBlk) void kb_combine(LayerTB L) {
+  const int t = blockIdx.x;
+  const int h0 = (blockIdx.y * kBlk + threadIdx.x) * 8;
+  if (h0 >= L.H) return;
+  const int P = L.T * L.k;
+  const int npos = P + L.S * L.T;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < L.k; ++j) {
+    const float w = L.wts[(size_t)t * L.k + j];
+    int pos = L.pos_of[(size_t)t * L.k + j];
+    pos = pos < 0 ? 0 : (pos >= npos ? npos - 1 : pos);
+    const float4* yp = reinterpret_cast<const float4*>(L.y + (size_t)pos * L.H + h0);
+    const float4 a = yp[0], b = yp[1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(w, v[i], acc[i]);
+  }
+  if (L.S) {
+    const float4* yp = reinterpret_cast<const float4*>(L.y + (size_t)(P + t) * L.H + h0);
+    const float4 a = yp[0], b = yp[1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+  }
+  const size_t o = (size_t)t * L.H + h0;
+  if (L.residual) {
+    const uint4 rv = *reinterpret_cast<const uint4*>(L.residual + o);
+    const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      acc[2 * d] += bf16_to_f32(rw[d] & 0xFFFFu);
+      acc[2 * d + 1] += bf16_to_f32(rw[d] >> 16);
+    }
+  }
+  uint32_t ow[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    ow[d] = (uint32_t)f32_to_bf16(acc[2 * d]) | ((uint32_t)f32_to_bf16(acc[2 * d + 1]) << 16);
+  const uint4 ov = {ow[0], ow[1], ow[2], ow[3]};
+  *reinterpret_cast<uint4*>(L.out + o) = ov;
+  if (L.trace) *reinterpret_cast<uint4*>(L.trace + o) = ov;
+}
+
+// ---------------------------------------------------------------- rmsnorm
+// xn[t] = bf16(h[t] * gamma / sqrt(mean(h[t]^2) + eps)), one workgroup per
+// token, the same reduction order as the single-token prologue.
+constexpr int kMaxChunksPerThread = 8192 / 8 / kBlk;
+__global__ __launch_bounds__(kBlk) void kb_rmsnorm(const uint16_t* __restrict__ h,
+                                                   const uint16_t* __restrict__ gamma, float eps,
+                                                   int H, uint16_t* __restrict__ xn) {
+  __shared__ float red[kWv];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const uint4* x16 = reinterpret_cast<const uint4*>(h + (size_t)t * H);
+  const uint4* g16 = reinterpret_cast<const uint4*>(gamma);
+  const int nch = H / 8;
+  uint4 v[kMaxChunksPerThread], g[kMaxChunksPerThread];
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerThread; ++i) {
+    const int c = tid + i * kBlk;
+    const int cc = c < nch ? c : nch - 1;
+    v[i] = x16[cc];
+    g[i] = g16[cc];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerThread; ++i) {
+    const int c = tid + i * kBlk;
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    float part = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float a = bf16_to_f32(w[d] & 0xFFFFu), b = bf16_to_f32(w[d] >> 16);
+      part = __builtin_fmaf(a, a, part);
+      part = __builtin_fmaf(b, b, part);
+    }
+    ss += c < nch ? part : 0.f;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave_id()] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWv; ++w) tot += red[w];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  uint4* o16 = reinterpret_cast<uint4*>(xn + (size_t)t * H);
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerThread; ++i) {
+    const int c = tid + i * kBlk;
+    if (c < nch) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+      uint32_t ov[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float a = bf16_to_f32(w[d] & 0xFFFFu) * inv * bf16_to_f32(gw[d] & 0xFFFFu);
+        const float b = bf16_to_f32(w[d] >> 16) * inv * bf16_to_f32(gw[d] >> 16);
+        ov[d] = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+      }
+      const uint4 o = {ov[0], ov[1], ov[2], ov[3]};
+      o16[c] = o;
+    }
+  }
+}
+
+constexpr int kGroupedBlocksPerCU = 8;
+constexpr int kNumCUs = 256;
+
+}  // namespace
+
+hipError_t launch_router_tb(const LayerTB& L, hipStream_t s) {
+  const int n_et = (L.E + kTileRows - 1) / kTileRows;
+  const int nw = n_et * L.KS;
+  hipLaunchKernelGGL(kb_router, dim3((nw + kWv - 1) / kWv), dim3(kBlk), 0, s, L, n_et);
+  return hipPeekAtLastError();
+}
+
+hipError_t launch_topk_tb(const LayerTB& L, hipStream_t s) {
+  hipLaunchKernelGGL(kb_topk, dim3(L.T), dim3(kTopkBlock), 0, s, L);
+  return hipPeekAtLastError();
+}
+
+hipError_t launch_group_tb(const LayerTB& L, hipStream_t s) {
+  hipLaunchKernelGGL(kb_group, dim3(1), dim3(kGroupBlock), 0, s, L);
+  return hipPeekAtLastError();
+}
+
+hipError_t launch_gateup_tb(const LayerTB& L, hipStream_t s) {
+  hipLaunchKernelGGL(kb_gateup, dim3(kNumCUs * kGroupedBlocksPerCU), dim3(kBlk), 0, s, L);
+  return hipPeekAtLastError();
+}
+
+hipError_t launch_down_tb(const LayerTB& L, hipStream_t s) {
+  hipLaunchKernelGGL(kb_down, dim3(kNumCUs * kGroupedBlocksPerCU), dim3(kBlk), 0, s, L);
+  return hipPeekAtLastError();
+}
+
+hipError_t launch_combine_tb(const LayerTB& L, hipStream_t s) {
+  const int chunks = (L.H + 8 * kBlk - 1) / (8 * kBlk);
+  hipLaunchKernelGGL(kb_combine, dim3(L.T, chunks), dim3(kBlk), 0, s, L);
+  return hipPeekAtLastError();
+}
+
+hipError_t launch_rmsnorm_tb(const uint16_t* h, const uint16_t* gamma, float eps, int T, int H,
+                             uint16_t* xn, hipStream_t s) {
+  hipLaunchKernelGGL(kb_rmsnorm, dim3(T), dim3(kBlk), 0, s, h, gamma, eps, H, xn);
+  return hipPeekAtLastError();
+}
+
+}  // namespace moe

@@ -70,6 +70,57 @@ hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* 
                             float* act, hipStream_t s);
 hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s);
 
+// ---- 2 <= T <= 64 path ------------------------------------------------------
+
+struct LayerTB {
+  int T, H, E, k, F, S;
+  int KS;                     // router K splits (H % (128 KS) == 0)
+  // inputs
+  const uint16_t* x;          // bf16 [T][H] MoE input
+  const uint16_t* residual;   // bf16 [T][H] or null
+  uint16_t* out;              // bf16 [T][H]
+  uint16_t* trace;            // optional copy of out
+  // weights
+  const uint16_t* router_w;
+  const uint8_t *g_codes, *g_scales, *u_codes, *u_scales, *d_codes, *d_scales;
+  const uint8_t *sg_codes, *sg_scales, *su_codes, *su_scales, *sd_codes, *sd_scales;
+  // workspace
+  float* part;                // [KS][T][E] partial router logits
+  int32_t* idx;               // [T][k]
+  float* wts;                 // [T][k]
+  int32_t* ginfo;             // [0]: number of groups (active experts + shared)
+  int32_t* g_expert;          // [E + 1] expert of each group (E: the shared expert)
+  int32_t* g_start;           // [E + 1] first sorted position of the group
+  int32_t* g_count;           // [E + 1] pairs in the group
+  int32_t* order;             // [T k + T] pair id at each sorted position
+  int32_t* pos_of;            // [T k] sorted position of pair t k + j
+  uint16_t* act_hi;           // [T k + T][F] bf16 leading part of silu(g) u
+  uint16_t* act_lo;           // [T k + T][F] bf16 remainder
+  float* y;                   // [T k + T][H] expert outputs per sorted pair
+  // optional user outputs
+  float* logits_out;          // [T][E]
+  int32_t* idx_out;           // [T][k]
+  float* w_out;               // [T][k]
+  int32_t* offsets_out;       // [E + 1] grouping offsets
+  int32_t* pairs_out;         // [T k] pair ids sorted by expert
+};
+
+// Router K splits for hidden size H: the largest KS <= 16 with H % (128 KS) == 0.
+inline int router_splits(int H) {
+  int ks = 16;
+  while (ks > 1 && H % (128 * ks)) --ks;
+  return ks;
+}
+
+hipError_t launch_router_tb(const LayerTB& L, hipStream_t s);
+hipError_t launch_topk_tb(const LayerTB& L, hipStream_t s);
+hipError_t launch_group_tb(const LayerTB& L, hipStream_t s);
+hipError_t launch_gateup_tb(const LayerTB& L, hipStream_t s);
+hipError_t launch_down_tb(const LayerTB& L, hipStream_t s);
+hipError_t launch_combine_tb(const LayerTB& L, hipStream_t s);
+hipError_t launch_rmsnorm_tb(const uint16_t* h, const uint16_t* gamma, float eps, int T, int H,
+                             uint16_t* xn, hipStream_t s);
+
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace moe

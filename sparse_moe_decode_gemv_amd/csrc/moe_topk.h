@@ -1,0 +1,139 @@
+// Top-k + softmax of one token's router logits by one 256-thread workgroup
+// (shared by the single-token and the batched paths).
+#pragma once
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// Top-k + softmax by one workgroup (E <= 1024, k <= 32).  Logits become
+// order-preserving 32-bit keys (-0 folded onto +0; a larger key is a larger
+// logit); thread t of the 256 holds experts 4t .. 4t+3 (lg[], already
+// loaded by the caller).
+//  1. Radix select, most significant byte first: four passes of a 256-bin
+//     LDS histogram over the keys that still match the chosen prefix, each
+//     followed by a wave scan from the top bin down, give the exact k-th
+//     largest key T and how many keys equal to T are needed (kr).
+//  2. Keys above T, and the kr lowest-indexed keys equal to T, are gathered.
+//  3. One wave ranks the k gathered (key, index) pairs by (key desc, index
+//     asc) and writes them in that order with their softmax weights.
+constexpr int kTopkBlock = 256;
+constexpr int kTopkPerThread = kMaxExperts / kTopkBlock;  // keys per thread
+
+struct TopkLds {
+  uint32_t hist[256];
+  uint32_t sel_key[kMaxTopK];
+  int32_t sel_idx[kMaxTopK];
+  uint32_t wave_eq[kTopkBlock / kWave];
+  int32_t pick[2];  // bin found by the current pass, count above it
+  int32_t nsel;
+};
+
+__device__ inline void topk_softmax_block(const float (&lg)[kTopkPerThread], int E, int k,
+                                          TopkLds& S, int32_t* idx, float* wts,
+                                          int32_t* idx_out, float* w_out) {
+  constexpr int KPT = kTopkPerThread;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  uint32_t key[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) key[i] = tid * KPT + i < E ? f32_order_key(lg[i]) : 0u;
+
+  uint32_t prefix = 0u;
+  int kr = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t decided = ~(0xFFFFFFFFu >> (8 * pass));  // bytes chosen so far
+    S.hist[tid] = 0u;
+    if (tid == 0) S.nsel = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const bool match = ((key[i] ^ prefix) & decided) == 0u;
+      if (match && key[i] != 0u) atomicAdd(&S.hist[(key[i] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wid == 0) {
+      // lane l holds bins 255-4l .. 252-4l (descending)
+      uint32_t cnt[4], tot = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        cnt[j] = S.hist[255 - 4 * lane - j];
+        tot += cnt[j];
+      }
+      const uint32_t incl = wave_incl_scan_u32(tot);
+      const uint64_t over = __ballot(incl >= (uint32_t)kr);
+      const int fl = (int)__builtin_ctzll(over);
+      if (lane == fl) {
+        uint32_t cum = incl - tot;
+        int bin = 0;
+        uint32_t above = 0u;
+        bool done = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!done && cum + cnt[j] >= (uint32_t)kr) {
+            bin = 255 - 4 * lane - j;
+            above = cum;
+            done = true;
+          }
+          cum += cnt[j];
+        }
+        S.pick[0] = bin;
+        S.pick[1] = (int)above;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)S.pick[0] << shift;
+    kr -= S.pick[1];
+    __syncthreads();  // pick[] and hist[] are rewritten by the next pass
+  }
+
+  // gather: keys above T, then the kr lowest-indexed keys equal to T
+  uint32_t neq = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) neq += key[i] == prefix ? 1u : 0u;
+  const uint32_t inc = wave_incl_scan_u32(neq);
+  if (lane == kWave - 1) S.wave_eq[wid] = inc;
+  __syncthreads();
+  uint32_t before = inc - neq;
+  for (int w = 0; w < wid; ++w) before += S.wave_eq[w];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    bool take = key[i] > prefix;
+    if (key[i] == prefix) {
+      take = before < (uint32_t)kr;
+      ++before;
+    }
+    if (take) {
+      const int pos = atomicAdd(&S.nsel, 1);
+      S.sel_key[pos] = key[i];
+      S.sel_idx[pos] = tid * KPT + i;
+    }
+  }
+  __syncthreads();
+  if (wid == 0) {
+    const bool act = lane < k;
+    const uint32_t mk = act ? S.sel_key[lane] : 0u;
+    const int mi = act ? S.sel_idx[lane] : 0;
+    int rank = 0;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t kj = S.sel_key[j];
+      const int ij = S.sel_idx[j];
+      rank += (kj > mk || (kj == mk && ij < mi)) ? 1 : 0;
+    }
+    const uint32_t top = wave_max_u32(mk);
+    const float l = f32_from_order_key(mk);
+    const float ex = act ? expf(l - f32_from_order_key(top)) : 0.f;
+    const float sum = wave_sum(ex);
+    if (act) {
+      const float w = ex / sum;
+      idx[rank] = mi;
+      wts[rank] = w;
+      if (idx_out) idx_out[rank] = mi;
+      if (w_out) w_out[rank] = w;
+    }
+  }
+}
+
+}  // namespace moe
