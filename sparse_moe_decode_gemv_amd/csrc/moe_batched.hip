@@ -246,72 +246,118 @@ __device__ __forceinline__ int token_of(const LayerTB& L, int pid) {
 }
 
 // ---------------------------------------------------------------- gate/up
-// Items (group, 16-row tile) in group-major order; wave w takes items w,
-// w + nwaves, ... so that waves running together read consecutive row tiles
-// of one expert.  Per 128-wide step a lane loads one 16-byte code chunk (and
-// its scale) of a gate row and of an up row, and 64 bytes of its token's
-// activations; the next step's loads are issued before this step's MFMAs.
-struct GuStep {
-  uint4 ag, au, b[4];
-  uint32_t sg, su;
+// Workgroup items (group, 4 consecutive 16-row tiles) in group-major order, so
+// the workgroups running together read consecutive rows of one expert.  The
+// four waves share the group's tokens: per K chunk of KC elements the
+// workgroup stages 16 tokens' activations in LDS (rows padded by 16 bytes so
+// that the 16 lanes of a ds_read_b128 phase hit distinct banks), double
+// buffered; each wave streams its own 16 gate and 16 up rows one chunk ahead
+// in registers (two statically named register sets).
+template <int KC>
+struct TokLds {
+  uint4 b[2][16][KC / 8 + 1];
 };
 
-__device__ __forceinline__ void gu_load(GuStep& S, const uint8_t* gc, const uint8_t* gs,
-                                        const uint8_t* uc, const uint8_t* us, const uint8_t* xr,
-                                        int blk) {
-  S.ag = ld_stream16(gc + (size_t)blk * 16);
-  S.au = ld_stream16(uc + (size_t)blk * 16);
-  S.sg = ld_stream8(gs + blk);
-  S.su = ld_stream8(us + blk);
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    S.b[s] = *reinterpret_cast<const uint4*>(xr + (size_t)(32 * blk + 8 * s) * 2);
-}
+// Up to two staged uint4 per thread and chunk, held in named registers.
+template <int PER>
+struct Stage {
+  u32x4 v0, v1;
+  __device__ __forceinline__ void load(const uint4* src) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(src);
+    v0 = p[0];
+    if (PER > 1) v1 = p[1];
+  }
+  __device__ __forceinline__ void store(uint4* dst) const {
+    u32x4* p = reinterpret_cast<u32x4*>(dst);
+    p[0] = v0;
+    if (PER > 1) p[1] = v1;
+  }
+};
 
-__device__ __forceinline__ void gu_compute(const GuStep& S, f32x4& cg, f32x4& cu) {
-  const float fg = e8m0_to_f32(S.sg), fu = e8m0_to_f32(S.su);
+template <int KC>
+struct GuRegs {
+  uint4 ag[KC / 128], au[KC / 128];
+  uint32_t sg[KC / 128], su[KC / 128];
+};
+
+template <int KC>
+__device__ __forceinline__ void gu_load_a(GuRegs<KC>& R, const uint8_t* gc, const uint8_t* gs,
+                                          const uint8_t* uc, const uint8_t* us, int c, int q) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const bf16x8 bv = as_bf16x8(S.b[s]);
-    cg = mfma(fp4x8_to_bf16(dword_of(S.ag, s), fg), bv, cg);
-    cu = mfma(fp4x8_to_bf16(dword_of(S.au, s), fu), bv, cu);
+  for (int kk = 0; kk < KC / 128; ++kk) {
+    const int blk = c * (KC / 32) + kk * 4 + q;
+    R.ag[kk] = ld_stream16(gc + (size_t)blk * 16);
+    R.au[kk] = ld_stream16(uc + (size_t)blk * 16);
+    R.sg[kk] = ld_stream8(gs + blk);
+    R.su[kk] = ld_stream8(us + blk);
   }
 }
 
+template <int KC>
+__device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, const uint4 (*bt)[KC / 8 + 1], int q,
+                                       int r, f32x4& cg, f32x4& cu) {
+#pragma unroll
+  for (int kk = 0; kk < KC / 128; ++kk) {
+    const float fg = e8m0_to_f32(R.sg[kk]), fu = e8m0_to_f32(R.su[kk]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 bv = as_bf16x8(bt[r][kk * 16 + 4 * q + s]);
+      cg = mfma(fp4x8_to_bf16(dword_of(R.ag[kk], s), fg), bv, cg);
+      cu = mfma(fp4x8_to_bf16(dword_of(R.au[kk], s), fu), bv, cu);
+    }
+  }
+}
+
+template <int KC>
 __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
-  const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+  __shared__ TokLds<KC> S;
+  constexpr int PER = KC / 128;  // staged uint4 per thread per chunk
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
   const int ng = L.ginfo[0];
-  const int tiles = L.F / kTileRows;
-  const int nitems = ng * tiles;
-  const int nblk = L.H / 32;  // MXFP4 blocks per gate/up row
-  const int nwaves = gridDim.x * kWv;
-  for (int it = blockIdx.x * kWv + wave_id(); it < nitems; it += nwaves) {
-    const int g = it / tiles, rt = it - g * tiles;
+  const int quads = L.F / (kTileRows * kWv);
+  const int nitems = ng * quads;
+  const int nch = L.H / KC;
+  const int sc = tid >> 4, sj = (tid & 15) * PER;  // staging: token row, first uint4
+  for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+    const int g = it / quads, rq = it - g * quads;
     const int e = L.g_expert[g], start = L.g_start[g], m = L.g_count[g];
     const bool sh = e >= L.E;
-    const size_t ebase = sh ? 0 : (size_t)e * L.F;
-    const int row = rt * kTileRows + r;
-    const size_t rsel = ebase + row;
+    const int row = (rq * kWv + wid) * kTileRows + r;
+    const size_t rsel = (sh ? 0 : (size_t)e * L.F) + row;
     const uint8_t* gc = (sh ? L.sg_codes : L.g_codes) + rsel * (L.H / 2);
     const uint8_t* gs = (sh ? L.sg_scales : L.g_scales) + rsel * (L.H / 32);
     const uint8_t* uc = (sh ? L.su_codes : L.u_codes) + rsel * (L.H / 2);
     const uint8_t* us = (sh ? L.su_scales : L.u_scales) + rsel * (L.H / 32);
     for (int n0 = 0; n0 < m; n0 += 16) {
-      const int c = n0 + r < m ? n0 + r : m - 1;
-      const int t = token_of(L, L.order[start + c]);
-      const uint8_t* xr = reinterpret_cast<const uint8_t*>(L.x + (size_t)t * L.H);
+      const int cs = n0 + sc < m ? n0 + sc : m - 1;
+      const uint4* xs = reinterpret_cast<const uint4*>(
+          L.x + (size_t)token_of(L, L.order[start + cs]) * L.H);
       f32x4 cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
-      GuStep A, B;
-      gu_load(A, gc, gs, uc, us, xr, q);
-      for (int kb = 0; kb < nblk; kb += 8) {
-        if (kb + 4 < nblk) gu_load(B, gc, gs, uc, us, xr, kb + 4 + q);
-        gu_compute(A, cg, cu);
-        if (kb + 4 >= nblk) break;
-        if (kb + 8 < nblk) gu_load(A, gc, gs, uc, us, xr, kb + 8 + q);
-        gu_compute(B, cg, cu);
+      GuRegs<KC> A0, A1;
+      Stage<PER> bst;
+      gu_load_a<KC>(A0, gc, gs, uc, us, 0, q);
+      bst.load(xs + sj);
+      bst.store(&S.b[0][sc][sj]);
+      __syncthreads();
+      for (int c = 0; c < nch; c += 2) {
+        if (c + 1 < nch) {
+          gu_load_a<KC>(A1, gc, gs, uc, us, c + 1, q);
+          bst.load(xs + (size_t)(c + 1) * (KC / 8) + sj);
+        }
+        gu_mma<KC>(A0, S.b[0], q, r, cg, cu);
+        if (c + 1 < nch) bst.store(&S.b[1][sc][sj]);
+        __syncthreads();
+        if (c + 1 >= nch) break;
+        if (c + 2 < nch) {
+          gu_load_a<KC>(A0, gc, gs, uc, us, c + 2, q);
+          bst.load(xs + (size_t)(c + 2) * (KC / 8) + sj);
+        }
+        gu_mma<KC>(A1, S.b[1], q, r, cg, cu);
+        if (c + 2 < nch) bst.store(&S.b[0][sc][sj]);
+        __syncthreads();
       }
       if (n0 + r < m) {
-        const size_t o = (size_t)(start + n0 + r) * L.F + rt * kTileRows + 4 * q;
+        const size_t o = (size_t)(start + n0 + r) * L.F + (rq * kWv + wid) * kTileRows + 4 * q;
         uint16_t hi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -332,60 +378,92 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
 }
 
 // ---------------------------------------------------------------- down
-struct DnStep {
-  uint4 a, bh[4], bl[4];
-  uint32_t sc;
+// Workgroup items (group, kDnWaves consecutive 16-row tiles of the hidden
+// size); per K chunk the workgroup stages the 16 pairs' a_hi and a_lo in LDS
+// (double buffered) and each wave streams its 16 down rows one chunk ahead.
+constexpr int kDnWaves = 8;
+constexpr int kDnBlock = kDnWaves * kWave;
+
+template <int KC>
+struct DnRegs {
+  uint4 a[KC / 128];
+  uint32_t sc[KC / 128];
 };
 
-__device__ __forceinline__ void dn_load(DnStep& S, const uint8_t* dc, const uint8_t* ds,
-                                        const uint8_t* ah, const uint8_t* al, int blk) {
-  S.a = ld_stream16(dc + (size_t)blk * 16);
-  S.sc = ld_stream8(ds + blk);
+template <int KC>
+__device__ __forceinline__ void dn_load_a(DnRegs<KC>& R, const uint8_t* dc, const uint8_t* ds, int c,
+                                          int q) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    S.bh[s] = *reinterpret_cast<const uint4*>(ah + (size_t)(32 * blk + 8 * s) * 2);
-    S.bl[s] = *reinterpret_cast<const uint4*>(al + (size_t)(32 * blk + 8 * s) * 2);
+  for (int kk = 0; kk < KC / 128; ++kk) {
+    const int blk = c * (KC / 32) + kk * 4 + q;
+    R.a[kk] = ld_stream16(dc + (size_t)blk * 16);
+    R.sc[kk] = ld_stream8(ds + blk);
   }
 }
 
-__device__ __forceinline__ void dn_compute(const DnStep& S, f32x4& acc) {
-  const float f = e8m0_to_f32(S.sc);
+template <int KC>
+__device__ __forceinline__ void dn_mma(const DnRegs<KC>& R, const uint4 (*bh)[KC / 8 + 1],
+                                       const uint4 (*bl)[KC / 8 + 1], int q, int r, f32x4& acc) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const bf16x8 av = fp4x8_to_bf16(dword_of(S.a, s), f);
-    acc = mfma(av, as_bf16x8(S.bh[s]), acc);
-    acc = mfma(av, as_bf16x8(S.bl[s]), acc);
+  for (int kk = 0; kk < KC / 128; ++kk) {
+    const float f = e8m0_to_f32(R.sc[kk]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 av = fp4x8_to_bf16(dword_of(R.a[kk], s), f);
+      acc = mfma(av, as_bf16x8(bh[r][kk * 16 + 4 * q + s]), acc);
+      acc = mfma(av, as_bf16x8(bl[r][kk * 16 + 4 * q + s]), acc);
+    }
   }
 }
 
-__global__ __launch_bounds__(kBlk) void kb_down(LayerTB L) {
-  const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+template <int KC>
+__global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
+  __shared__ TokLds<KC> Sh, Sl;
+  constexpr int PER = KC / 128;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
   const int ng = L.ginfo[0];
-  const int tiles = L.H / kTileRows;
-  const int nitems = ng * tiles;
-  const int nblk = L.F / 32;  // MXFP4 blocks per down row
-  const int nwaves = gridDim.x * kWv;
-  for (int it = blockIdx.x * kWv + wave_id(); it < nitems; it += nwaves) {
-    const int g = it / tiles, rt = it - g * tiles;
+  const int slabs = L.H / (kTileRows * kDnWaves);
+  const int nitems = ng * slabs;
+  const int nch = L.F / KC;
+  const bool st_lo = tid >= 256;  // staging: threads 0..255 stage a_hi, 256..511 a_lo
+  const int sc = (tid & 255) >> 4, sj = (tid & 15) * PER;
+  for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+    const int g = it / slabs, sb = it - g * slabs;
     const int e = L.g_expert[g], start = L.g_start[g], m = L.g_count[g];
     const bool sh = e >= L.E;
+    const int rt = sb * kDnWaves + wid;
     const size_t rsel = (sh ? 0 : (size_t)e * L.H) + rt * kTileRows + r;
     const uint8_t* dc = (sh ? L.sd_codes : L.d_codes) + rsel * (L.F / 2);
     const uint8_t* ds = (sh ? L.sd_scales : L.d_scales) + rsel * (L.F / 32);
     for (int n0 = 0; n0 < m; n0 += 16) {
-      const int c = n0 + r < m ? n0 + r : m - 1;
-      const size_t ao = (size_t)(start + c) * L.F;
-      const uint8_t* ah = reinterpret_cast<const uint8_t*>(L.act_hi + ao);
-      const uint8_t* al = reinterpret_cast<const uint8_t*>(L.act_lo + ao);
+      const int cs = n0 + sc < m ? n0 + sc : m - 1;
+      const uint4* as = reinterpret_cast<const uint4*>((st_lo ? L.act_lo : L.act_hi) +
+                                                       (size_t)(start + cs) * L.F);
+      uint4 (*sbuf0)[KC / 8 + 1] = st_lo ? Sl.b[0] : Sh.b[0];
+      uint4 (*sbuf1)[KC / 8 + 1] = st_lo ? Sl.b[1] : Sh.b[1];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      DnStep A, B;
-      dn_load(A, dc, ds, ah, al, q);
-      for (int kb = 0; kb < nblk; kb += 8) {
-        if (kb + 4 < nblk) dn_load(B, dc, ds, ah, al, kb + 4 + q);
-        dn_compute(A, acc);
-        if (kb + 4 >= nblk) break;
-        if (kb + 8 < nblk) dn_load(A, dc, ds, ah, al, kb + 8 + q);
-        dn_compute(B, acc);
+      DnRegs<KC> A0, A1;
+      Stage<PER> bst;
+      dn_load_a<KC>(A0, dc, ds, 0, q);
+      bst.load(as + sj);
+      bst.store(&sbuf0[sc][sj]);
+      __syncthreads();
+      for (int c = 0; c < nch; c += 2) {
+        if (c + 1 < nch) {
+          dn_load_a<KC>(A1, dc, ds, c + 1, q);
+          bst.load(as + (size_t)(c + 1) * (KC / 8) + sj);
+        }
+        dn_mma<KC>(A0, Sh.b[0], Sl.b[0], q, r, acc);
+        if (c + 1 < nch) bst.store(&sbuf1[sc][sj]);
+        __syncthreads();
+        if (c + 1 >= nch) break;
+        if (c + 2 < nch) {
+          dn_load_a<KC>(A0, dc, ds, c + 2, q);
+          bst.load(as + (size_t)(c + 2) * (KC / 8) + sj);
+        }
+        dn_mma<KC>(A1, Sh.b[1], Sl.b[1], q, r, acc);
+        if (c + 2 < nch) bst.store(&sbuf0[sc][sj]);
+        __syncthreads();
       }
       if (n0 + r < m) {
         float4 v;
@@ -509,7 +587,8 @@ __global__ __launch_bounds__(kBlk) void kb_rmsnorm(const uint16_t* __restrict__ 
   }
 }
 
-constexpr int kGroupedBlocksPerCU = 8;
+constexpr int kGroupedBlocksPerCU = 4;
+constexpr int kDownBlocksPerCU = 2;
 constexpr int kNumCUs = 256;
 
 }  // namespace
@@ -532,12 +611,17 @@ hipError_t launch_group_tb(const LayerTB& L, hipStream_t s) {
 }
 
 hipError_t launch_gateup_tb(const LayerTB& L, hipStream_t s) {
-  hipLaunchKernelGGL(kb_gateup, dim3(kNumCUs * kGroupedBlocksPerCU), dim3(kBlk), 0, s, L);
+  // H % 256 == 0 always; 256-element chunks
+  hipLaunchKernelGGL(kb_gateup<256>, dim3(kNumCUs * kGroupedBlocksPerCU), dim3(kBlk), 0, s, L);
   return hipPeekAtLastError();
 }
 
 hipError_t launch_down_tb(const LayerTB& L, hipStream_t s) {
-  hipLaunchKernelGGL(kb_down, dim3(kNumCUs * kGroupedBlocksPerCU), dim3(kBlk), 0, s, L);
+  const dim3 grid(kNumCUs * kDownBlocksPerCU);
+  if (L.F % 256 == 0)
+    hipLaunchKernelGGL(kb_down<256>, grid, dim3(kDnBlock), 0, s, L);
+  else
+    hipLaunchKernelGGL(kb_down<128>, grid, dim3(kDnBlock), 0, s, L);
   return hipPeekAtLastError();
 }
 
