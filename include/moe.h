@@ -28,7 +28,9 @@
  *    scale 2^(b-127) per 32 consecutive elements of a row, b = 0xFF is NaN):
  *      codes  uint8 [R][C/2]  element 2i in bits 3:0 of byte i, 2i+1 in 7:4
  *      scales uint8 [R][C/32]
- *    codes must be 16-byte aligned.  The reduction dimension is the row:
+ *    codes must be 16-byte aligned, scales 4-byte aligned (kernels read
+ *    scales as aligned 32-bit words; rows are a multiple of 4 bytes long
+ *    for every accepted shape).  The reduction dimension is the row:
  *    C = H for gate/up, C = F for down.
  *  - Workspace: `ws` is a 16-byte aligned device buffer of at least
  *    moe_workspace_size() bytes.  Its first MOE_WS_COUNTER_BYTES bytes are
@@ -82,7 +84,7 @@ typedef struct {
 
 typedef struct {
   const uint8_t* codes;  /* [R][C/2], 16-byte aligned */
-  const uint8_t* scales; /* [R][C/32] */
+  const uint8_t* scales; /* [R][C/32], 4-byte aligned */
 } moe_mx_mat;
 
 typedef struct {

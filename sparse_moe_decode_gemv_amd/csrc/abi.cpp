@@ -120,6 +120,7 @@ int check_ws(const moe_shape* s, int32_t T, const void* ws, size_t ws_bytes) {
 
 int check_mat(const moe_mx_mat& m) {
   if (!m.codes || !m.scales || !aligned16(m.codes)) return MOE_ERR_INVALID_ARG;
+  if ((uintptr_t)m.scales & 3u) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -213,14 +214,13 @@ LayerTB make_layer_tb(const moe_shape* s, const moe_layer_weights* w, void* ws, 
 
 uint16_t* xn_tb(const moe_shape* s, void* ws, int T) { return (uint16_t*)((char*)ws + ws_tb(*s, T).xn); }
 
-// One full single-token layer: K1a, K1b, K2, K3 on one stream.
+// One full single-token layer: K1a (router + shared gate/up), K2 (top-k,
+// routed gate/up, shared down), K3 (down + combine) on one stream.
 int run_layer_t1(LayerT1& L, hipStream_t st) {
   hipError_t e = moe::launch_router_t1(L, true, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_topk_t1(L, true, st);
-  if (e != hipSuccess) return MOE_ERR_HIP;
   const uint16_t* xin = L.gamma ? L.xn : L.x;
-  e = moe::launch_gateup_t1(L, xin, L.idx, L.act, st);
+  e = moe::launch_gateup_t1(L, xin, nullptr, L.act, true, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_down_combine_t1(L, st));
 }
@@ -286,7 +286,7 @@ int moe_router_topk(const moe_shape* shape, const uint16_t* x, const uint16_t* r
     L.w_out = topk_w;
     L.logits_out = logits;
     if (moe::launch_router_t1(L, false, st) != hipSuccess) return MOE_ERR_HIP;
-    return hip_status(moe::launch_topk_t1(L, false, st));
+    return hip_status(moe::launch_topk_t1(L, st));
   }
   LayerTB L = make_layer_tb(shape, nullptr, ws, n_tokens);
   L.router_w = router_w;
@@ -309,7 +309,7 @@ int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const 
   if ((rc = check_ws(shape, n_tokens, ws, ws_bytes))) return rc;
   if (n_tokens > 1) return MOE_ERR_UNSUPPORTED;
   LayerT1 L = make_layer(shape, w, ws);
-  return hip_status(moe::launch_gateup_t1(L, x, topk_idx, act, (hipStream_t)stream));
+  return hip_status(moe::launch_gateup_t1(L, x, topk_idx, act, false, (hipStream_t)stream));
 }
 
 int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,

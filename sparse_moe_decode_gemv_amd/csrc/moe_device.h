@@ -28,6 +28,35 @@ __device__ __forceinline__ uint4 ld_stream16(const uint8_t* p) {
 __device__ __forceinline__ uint32_t ld_stream8(const uint8_t* p) {
   return __builtin_nontemporal_load(p);
 }
+// The 32-bit word that holds byte b of a 4-byte aligned row (the caller
+// extracts the byte with byte_of(w, b & 3)).  Used for scale bytes that stay
+// in flight across a loop iteration: a byte load's result gets a
+// zero-extension that the compiler may place before the loop's back edge,
+// which waits for the load there.
+__device__ __forceinline__ uint32_t ld_stream_word_of(const uint8_t* row, int b) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row) + (b >> 2));
+}
+// Raw buffer access: a descriptor (base, size in bytes) held in scalar
+// registers, a per-lane 32-bit offset and a wave-uniform scalar offset.
+// Used where many rows are in flight at once: every row then needs one
+// scalar offset instead of a 64-bit vector address.  Reads at or past
+// `bytes` return zero.
+constexpr int kBufDataFormat = 0x00020000;  // descriptor word 3 for raw dword data (gfx9)
+constexpr int kBufNT = 2;                   // cache policy: nontemporal
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufDataFormat);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kBufNT);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kBufNT);
+}
+__device__ __forceinline__ uint32_t byte_of(uint32_t w, int byte) {
+  return __builtin_amdgcn_ubfe(w, 8 * byte, 8);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
@@ -109,6 +138,19 @@ __device__ __forceinline__ float group_sum_last(float v, int width) {
   if (width >= 16) v += dpp_term<0x140, 0xF>(v);  // row_mirror
   if (width >= 32) v += dpp_term<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
   if (width >= 64) v += dpp_term<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// group_sum_last for a width known at compile time.
+template <int W>
+__device__ __forceinline__ float group_sum_last_c(float v) {
+  static_assert(W >= 4 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  v += dpp_term<0xB1, 0xF>(v);
+  v += dpp_term<0x4E, 0xF>(v);
+  if (W >= 8) v += dpp_term<0x141, 0xF>(v);
+  if (W >= 16) v += dpp_term<0x140, 0xF>(v);
+  if (W >= 32) v += dpp_term<0x142, 0xA>(v);
+  if (W >= 64) v += dpp_term<0x143, 0xC>(v);
   return v;
 }
 

@@ -62,12 +62,14 @@ struct LayerT1 {
   float* w_out;
 };
 
-// K1a router (+ shared gate/up), K1b top-k (+ shared down), K2 gate/up,
-// K3 down + combine; with_shared = false skips the shared-expert work.
+// K1a router (+ shared gate/up), K2 top-k when idx is null (+ shared down
+// when asked) and gate/up, K3 down + combine; launch_topk_t1 is the
+// stand-alone top-k of the router entry point.  with_shared = false skips
+// the shared-expert work.
 hipError_t launch_router_t1(const LayerT1& L, bool with_shared, hipStream_t s);
-hipError_t launch_topk_t1(const LayerT1& L, bool with_shared, hipStream_t s);
+hipError_t launch_topk_t1(const LayerT1& L, hipStream_t s);
 hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* idx,
-                            float* act, hipStream_t s);
+                            float* act, bool with_shared_down, hipStream_t s);
 hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s);
 
 // ---- 2 <= T <= 64 path ------------------------------------------------------

@@ -1,15 +1,15 @@
-// Single-token (batch 1) decode layer: four kernels per layer, one stream.
+// Single-token (batch 1) decode layer: three kernels per layer, one stream.
 //
 //  K1a router GEMV over all E rows (one wave per row, every load of the row
 //      in flight at once).  Spare workgroups stream the shared expert's
 //      gate/up rows: the shared expert does not depend on routing (the pages
 //      run it beside the selected experts: page "AI手搓1.2万行代码榨干GB300!…",
 //      section 02; smzdm page, section "四步改造").
-//  K1b top-k + softmax in workgroup 0 (radix select); the other workgroups run
-//      the shared expert's down projection, so the selection latency is
-//      spent under shared-expert bytes.
-//  K2  gate/up GEMVs of the k selected experts with fused MXFP4 dequant and
-//      SiLU gating -> fp32 activations.
+//  K2  top-k + softmax (radix select) in every gate/up workgroup, then the
+//      gate/up GEMVs of the k selected experts with fused MXFP4 dequant and
+//      SiLU gating -> fp32 activations; the first workgroups run the shared
+//      expert's down projection meanwhile, so the selection latency is spent
+//      under shared-expert bytes.
 //  K3  down GEMVs of the selected experts, router-weighted combine with the
 //      shared output (weight 1) and residual add -> bf16.  One 16-wave
 //      workgroup per CU owns a slab of output rows, wave w streams slot w's
@@ -125,38 +125,68 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, const ui
   __syncthreads();
 }
 
+// Plain x staging in two halves, so that other loads can be issued between
+// them: stage_x_load issues the global loads, stage_x_store writes LDS
+// (zero padding included) and ends with a barrier.
+struct XStage {
+  uint4 v[kChunksPerLane];
+};
+__device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int H, XStage& st) {
+  const uint4* x16 = reinterpret_cast<const uint4*>(x);
+  const int nch = H / 8;
+#pragma unroll
+  for (int i = 0; i < kChunksPerLane; ++i) {
+    const int c = threadIdx.x + i * kBlock;
+    st.v[i] = x16[c < nch ? c : nch - 1];
+  }
+}
+__device__ __forceinline__ void stage_x_store(const XStage& st, int H, uint32_t* x_lds) {
+  uint4* l16 = reinterpret_cast<uint4*>(x_lds);
+  const int nch = H / 8;
+#pragma unroll
+  for (int i = 0; i < kChunksPerLane; ++i) {
+    const int c = threadIdx.x + i * kBlock;
+    l16[c] = keep_or_zero(c < nch, st.v[i]);
+  }
+  __syncthreads();
+}
+
 // -------------------------------------------------------------------------
 // Router rows: one wave per row; the row's 16-byte chunks are strided over
-// the lanes and every chunk is requested before the first dot product.  The
-// loop always covers kMaxChunks chunks so that no load is conditional:
-// chunks past the row end load the row's last chunk again (in bounds) and
-// meet the zero padding of x in LDS.
-__device__ void router_rows(const LayerT1& L, const uint32_t* x_lds, int gw, int nw) {
+// the lanes and every chunk is requested before the first dot product (and
+// before x is staged).  The loads always cover kMaxChunks chunks so that no
+// load is conditional: chunks past the row end load the row's last chunk
+// again (in bounds) and meet the zero padding of x in LDS.
+struct RouterRow {
+  uint4 v[kMaxChunks / kWave];
+};
+__device__ __forceinline__ void router_row_load(const LayerT1& L, int e, RouterRow& R) {
   const int lane = threadIdx.x & 63;
   const int nch = L.H / 8;
+  const uint8_t* row = reinterpret_cast<const uint8_t*>(L.router_w + (size_t)e * L.H);
+#pragma unroll
+  for (int i = 0; i < kMaxChunks / kWave; ++i) {
+    const int c = i * kWave + lane;
+    R.v[i] = ld_stream16(row + (size_t)(c < nch ? c : nch - 1) * 16);
+  }
+}
+__device__ __forceinline__ void router_row_finish(const LayerT1& L, int e, const RouterRow& R,
+                                                  const uint32_t* x_lds) {
+  const int lane = threadIdx.x & 63;
   const uint4* xl = reinterpret_cast<const uint4*>(x_lds);
-  for (int e = gw; e < L.E; e += nw) {
-    const uint8_t* row = reinterpret_cast<const uint8_t*>(L.router_w + (size_t)e * L.H);
-    uint4 v[kMaxChunks / kWave];
+  float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxChunks / kWave; ++i) {
-      const int c = i * kWave + lane;
-      v[i] = ld_stream16(row + (size_t)(c < nch ? c : nch - 1) * 16);
-    }
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxChunks / kWave; ++i) {
-      const uint4 xv = xl[i * kWave + lane];
-      a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[i].x), as_bf16x2(xv.x), a0, false);
-      a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[i].y), as_bf16x2(xv.y), a1, false);
-      a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[i].z), as_bf16x2(xv.z), a0, false);
-      a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[i].w), as_bf16x2(xv.w), a1, false);
-    }
-    const float s = group_sum_last(a0 + a1, kWave);
-    if (lane == kWave - 1) {
-      L.logits[e] = s;
-      if (L.logits_out) L.logits_out[e] = s;
-    }
+  for (int i = 0; i < kMaxChunks / kWave; ++i) {
+    const uint4 xv = xl[i * kWave + lane];
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(R.v[i].x), as_bf16x2(xv.x), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(R.v[i].y), as_bf16x2(xv.y), a1, false);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(R.v[i].z), as_bf16x2(xv.z), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(R.v[i].w), as_bf16x2(xv.w), a1, false);
+  }
+  const float s = group_sum_last(a0 + a1, kWave);
+  if (lane == kWave - 1) {
+    L.logits[e] = s;
+    if (L.logits_out) L.logits_out[e] = s;
   }
 }
 
@@ -198,7 +228,7 @@ struct GateUp {
     for (int i = 0; i < BPL; ++i) {
       const int b = col + lanes * i;
       c[i] = ld_stream16(cb + (size_t)b * 16);
-      sc[i] = ld_stream8(sb + b);
+      sc[i] = ld_stream_word_of(sb, b);
     }
   }
   __device__ __forceinline__ void finish(const GateUpJob& J, const uint32_t* x_lds, int t,
@@ -216,7 +246,12 @@ struct GateUp {
         xv[4 * q + 2] = v.z;
         xv[4 * q + 3] = v.w;
       }
-      acc = __builtin_fmaf(block_dot_bf16(c[i], xv), e8m0_to_f32(sc[i]), acc);
+      // rows are 4-byte multiples and lanes % 4 == 0: block b's byte is b & 3
+      const float scale = e8m0_to_f32(byte_of(sc[i], (col + lanes * i) & 3));
+      acc = __builtin_fmaf(block_dot_bf16(c[i], xv), scale, acc);
+      // keep the x reads of later blocks from being hoisted: shorter live
+      // ranges give three waves per SIMD instead of two
+      __builtin_amdgcn_sched_barrier(0);
     }
     acc = group_sum_last(acc, lanes);
     const float up = __shfl_xor(acc, 32, kWave);
@@ -228,22 +263,33 @@ struct GateUp {
   }
 };
 
+// Tasks first, first + stride, ... below ntask; the first task's weights are
+// already in (ca, sa) (requested by the caller ahead of the x staging).  Task
+// i + 1 is requested before task i is reduced.  The loop runs an exact trip
+// count and the last one or two tasks are peeled, so no load sits under a
+// branch that rejoins: at such a join the compiler's wait counts assume the
+// path without the load and would wait for the newer loads as well.
 template <int BPL>
 __device__ void gateup_tasks(const GateUp<BPL>& g, const GateUpJob& J, const uint32_t* x_lds,
-                             int ntask, int first, int stride) {
-  uint4 ca[BPL], cb[BPL];
-  uint32_t sa[BPL], sb[BPL];
-  int t = first;
-  if (t < ntask) g.load(J, t, ca, sa);
-  while (t < ntask) {
-    const int t1 = t + stride;
-    if (t1 < ntask) g.load(J, t1, cb, sb);
+                             int ntask, int first, int stride, uint4 (&ca)[BPL],
+                             uint32_t (&sa)[BPL]) {
+  if (first >= ntask) return;
+  const int n = (ntask - first + stride - 1) / stride;
+  uint4 cb[BPL];
+  uint32_t sb[BPL];
+  int t = first, i = 0;
+  for (; i + 2 < n; i += 2, t += 2 * stride) {
+    g.load(J, t + stride, cb, sb);
     g.finish(J, x_lds, t, ca, sa);
-    if (t1 >= ntask) break;
-    const int t2 = t1 + stride;
-    if (t2 < ntask) g.load(J, t2, ca, sa);
-    g.finish(J, x_lds, t1, cb, sb);
-    t = t2;
+    g.load(J, t + 2 * stride, ca, sa);
+    g.finish(J, x_lds, t + stride, cb, sb);
+  }
+  if (n - i == 2) {
+    g.load(J, t + stride, cb, sb);
+    g.finish(J, x_lds, t, ca, sa);
+    g.finish(J, x_lds, t + stride, cb, sb);
+  } else {
+    g.finish(J, x_lds, t, ca, sa);
   }
 }
 
@@ -251,17 +297,23 @@ __device__ void gateup_tasks(const GateUp<BPL>& g, const GateUpJob& J, const uin
 // Down rows of one matrix D[H][F] against fp32 activations held in
 // registers; `lanes` lanes per row, BPL blocks per lane, 64/lanes rows per
 // load instruction.
-template <int BPL>
+// LANES > 0 fixes the lane count at compile time (shifts and a constant
+// reduction width); LANES = 0 takes it at run time.
+template <int BPL, int LANES = 0>
 struct DownLanes {
   int rig, col, lanes, rpw;
   float ar[BPL][32];
 
   __device__ void init_map(int lanes_) {
     const int lane = threadIdx.x & 63;
-    lanes = lanes_;
+    lanes = LANES ? LANES : lanes_;
     rig = lane / lanes;
     col = lane % lanes;
     rpw = kWave / lanes;
+  }
+  __device__ __forceinline__ float reduce(float v) const {
+    if (LANES) return group_sum_last_c<LANES ? LANES : 64>(v);
+    return group_sum_last(v, lanes);
   }
   __device__ void load_act(const float* a) {
     const float4* a16 = reinterpret_cast<const float4*>(a);
@@ -278,170 +330,296 @@ struct DownLanes {
       }
     }
   }
+  // Rows row0 .. row0 + rpw - 1 (row0 uniform across the wave; this lane's
+  // row is row0 + rig).  Addresses are a wave-uniform base plus a 32-bit
+  // lane offset, which keeps one scalar base per load instead of a 64-bit
+  // vector address (many rows are in flight at once).
   __device__ __forceinline__ void load_row(const uint8_t* codes, const uint8_t* scales, int F,
-                                           int row, uint4 (&c)[BPL], uint32_t (&sc)[BPL]) const {
-    const uint8_t* cb = codes + (size_t)row * (F / 2);
-    const uint8_t* sb = scales + (size_t)row * (F / 32);
+                                           int row0, uint4 (&c)[BPL], uint32_t (&sc)[BPL]) const {
+    const uint8_t* cb = codes + (size_t)row0 * (F / 2);
+    const uint8_t* sb = scales + (size_t)row0 * (F / 32);
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
-      const int b = col + lanes * i;
-      c[i] = ld_stream16(cb + (size_t)b * 16);
-      sc[i] = ld_stream8(sb + b);
+      const uint32_t b = (uint32_t)(col + lanes * i);
+      c[i] = ld_stream16(cb + ((uint32_t)rig * (uint32_t)(F / 2) + b * 16u));
+      sc[i] = ld_stream_word_of(sb + (uint32_t)rig * (uint32_t)(F / 32), (int)b);
+    }
+  }
+  // The same rows of one matrix given as buffer descriptors (codes, scales):
+  // the row offset goes in a scalar register, the lane offset in one vector
+  // register shared by every row.
+  __device__ __forceinline__ void load_row_buf(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                               int F, int row0, uint4 (&c)[BPL],
+                                               uint32_t (&sc)[BPL]) const {
+    const uint32_t soc = (uint32_t)row0 * (uint32_t)(F / 2);
+    const uint32_t sos = (uint32_t)row0 * (uint32_t)(F / 32);
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const uint32_t b = (uint32_t)(col + lanes * i);
+      c[i] = buf_ld16(rc, (uint32_t)rig * (uint32_t)(F / 2) + b * 16u, soc);
+      sc[i] = buf_ld4(rs, ((uint32_t)rig * (uint32_t)(F / 32) + b) & ~3u, sos);
     }
   }
   __device__ __forceinline__ float dot(const uint4 (&c)[BPL], const uint32_t (&sc)[BPL]) const {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < BPL; ++i)
-      acc = __builtin_fmaf(block_dot_f32(c[i], ar[i]), e8m0_to_f32(sc[i]), acc);
+      acc = __builtin_fmaf(block_dot_f32(c[i], ar[i]),
+                           e8m0_to_f32(byte_of(sc[i], (col + lanes * i) & 3)), acc);
     return acc;
   }
 };
 
 // -------------------------------------------------------------------------
-// K1a: router rows (+ shared gate/up in the workgroups past n_router).
+// K1a: router rows (+ shared gate/up in the workgroups past n_router).  Each
+// wave requests its first weights before x is staged (RMSNorm'ed for the
+// stack), so that the weight stream starts at once.
 template <int BPLH>
 __global__ __launch_bounds__(kBlock) void k1_router(LayerT1 L, int n_router, int gu_lanes) {
   __shared__ __align__(16) uint32_t x_lds[kMaxH / 2];
   __shared__ float red[kWaves];
   const int wid = wave_id();
-  stage_x(L.x, L.gamma, L.eps, L.H, x_lds, red,
-          (L.gamma && blockIdx.x == 0) ? L.xn : nullptr);
   if ((int)blockIdx.x < n_router) {
-    router_rows(L, x_lds, blockIdx.x * kWaves + wid, n_router * kWaves);
+    const int gw = blockIdx.x * kWaves + wid, nw = n_router * kWaves;
+    RouterRow R;
+    const int e0 = gw < L.E ? gw : L.E - 1;
+    router_row_load(L, e0, R);
+    stage_x(L.x, L.gamma, L.eps, L.H, x_lds, red, (L.gamma && blockIdx.x == 0) ? L.xn : nullptr);
+    if (gw < L.E) router_row_finish(L, gw, R, x_lds);
+    for (int e = gw + nw; e < L.E; e += nw) {
+      router_row_load(L, e, R);
+      router_row_finish(L, e, R, x_lds);
+    }
     return;
   }
   GateUp<BPLH> g;
   g.init(gu_lanes, L.F);
   const GateUpJob J{L.sg_codes, L.sg_scales, L.su_codes, L.su_scales, nullptr, L.H, L.F,
                     L.act + (size_t)L.k * L.F};
-  gateup_tasks(g, J, x_lds, g.tps, (blockIdx.x - n_router) * kWaves + wid,
-               (gridDim.x - n_router) * kWaves);
+  const int first = (blockIdx.x - n_router) * kWaves + wid;
+  uint4 ca[BPLH];
+  uint32_t sa[BPLH];
+  g.load(J, first < g.tps ? first : g.tps - 1, ca, sa);
+  stage_x(L.x, L.gamma, L.eps, L.H, x_lds, red, nullptr);
+  gateup_tasks(g, J, x_lds, g.tps, first, (gridDim.x - n_router) * kWaves, ca, sa);
 }
 
-// K1b: top-k + softmax in workgroup 0; shared down rows -> y_shared in the
-// others, kRowsK1b row groups per wave with all loads in flight.
-constexpr int kRowsK1b = 8;
+// Shared expert's down rows -> y_shared: wave gw takes kRowsSd row groups
+// with all their loads in flight.
+constexpr int kRowsSd = 8;
 template <int BPLF>
-__global__ __launch_bounds__(kBlock) void k1_topk(LayerT1 L, int dn_lanes) {
+__device__ void shared_down_rows(const LayerT1& L, int dn_lanes, int gw) {
+  DownLanes<BPLF> d;
+  d.init_map(dn_lanes);
+  d.load_act(L.act + (size_t)L.k * L.F);
+  const int ngroups = L.H / d.rpw;
+  const int g0 = gw * kRowsSd;
+  uint4 c[kRowsSd][BPLF];
+  uint32_t sc[kRowsSd][BPLF];
+#pragma unroll
+  for (int j = 0; j < kRowsSd; ++j) {
+    const int g = g0 + j < ngroups ? g0 + j : ngroups - 1;
+    d.load_row(L.sd_codes, L.sd_scales, L.F, g * d.rpw, c[j], sc[j]);
+  }
+  float v[kRowsSd];
+#pragma unroll
+  for (int j = 0; j < kRowsSd; ++j) v[j] = d.dot(c[j], sc[j]);
+#pragma unroll
+  for (int j = 0; j < kRowsSd; ++j) v[j] = group_sum_last(v[j], d.lanes);
+#pragma unroll
+  for (int j = 0; j < kRowsSd; ++j)
+    if (g0 + j < ngroups && d.col == d.lanes - 1) L.y_shared[(g0 + j) * d.rpw + d.rig] = v[j];
+}
+
+// K1b (router-only entry point): top-k + softmax of the logits, one workgroup.
+__global__ __launch_bounds__(kBlock) void k1_topk(LayerT1 L) {
   __shared__ TopkLds tk;
-  if (blockIdx.x == 0) {
+  float lg[kTopkPerThread];
+#pragma unroll
+  for (int i = 0; i < kTopkPerThread; ++i) {
+    const int e = threadIdx.x * kTopkPerThread + i;
+    lg[i] = L.logits[e < L.E ? e : L.E - 1];
+  }
+  topk_softmax_block(lg, L.E, L.k, tk, L.idx, L.wts, L.idx_out, L.w_out);
+}
+
+// K2: routed gate/up of the k selected experts.  With idx == null the
+// experts are selected here: every gate/up workgroup runs the same top-k on
+// the router logits (deterministic, identical in every workgroup) and
+// workgroup n_sd publishes the indices and weights for K3 and the caller.
+// The first n_sd workgroups instead run the shared expert's down rows
+// (shared activations from K1a) -> y_shared: they need no routing, so they
+// are placed first and stream while the others select.
+template <int BPLH, int BPLF>
+__global__ __launch_bounds__(kBlock) void k2_gateup(LayerT1 L, const uint16_t* __restrict__ x,
+                                                    const int32_t* __restrict__ idx,
+                                                    float* __restrict__ act, int gu_lanes, int n_sd,
+                                                    int dn_lanes) {
+  __shared__ __align__(16) uint32_t x_lds[kMaxH / 2];
+  __shared__ int32_t e_lds[kMaxTopK];
+  __shared__ float w_lds[kMaxTopK];
+  __shared__ TopkLds tk;
+  const int wid = wave_id();
+  if ((int)blockIdx.x < n_sd) {
+    shared_down_rows<BPLF>(L, dn_lanes, (int)blockIdx.x * kWaves + wid);
+    return;
+  }
+  const int gb = blockIdx.x - n_sd;
+  XStage xs;
+  stage_x_load(x, L.H, xs);
+  if (idx) {
+    if (threadIdx.x < L.k) {
+      const int e = idx[threadIdx.x];
+      e_lds[threadIdx.x] = e < 0 ? 0 : (e >= L.E ? L.E - 1 : e);  // never address outside
+    }
+    __syncthreads();
+  } else {
     float lg[kTopkPerThread];
 #pragma unroll
     for (int i = 0; i < kTopkPerThread; ++i) {
       const int e = threadIdx.x * kTopkPerThread + i;
       lg[i] = L.logits[e < L.E ? e : L.E - 1];
     }
-    topk_softmax_block(lg, L.E, L.k, tk, L.idx, L.wts, L.idx_out, L.w_out);
-    return;
+    topk_softmax_block(lg, L.E, L.k, tk, e_lds, w_lds, nullptr, nullptr);
+    __syncthreads();
   }
-  const int wid = wave_id();
-  DownLanes<BPLF> d;
-  d.init_map(dn_lanes);
-  d.load_act(L.act + (size_t)L.k * L.F);
-  const int ngroups = L.H / d.rpw;
-  const int g0 = ((blockIdx.x - 1) * kWaves + wid) * kRowsK1b;
-  uint4 c[kRowsK1b][BPLF];
-  uint32_t sc[kRowsK1b][BPLF];
-#pragma unroll
-  for (int j = 0; j < kRowsK1b; ++j) {
-    const int g = g0 + j < ngroups ? g0 + j : ngroups - 1;
-    d.load_row(L.sd_codes, L.sd_scales, L.F, g * d.rpw + d.rig, c[j], sc[j]);
-  }
-  float v[kRowsK1b];
-#pragma unroll
-  for (int j = 0; j < kRowsK1b; ++j) v[j] = d.dot(c[j], sc[j]);
-#pragma unroll
-  for (int j = 0; j < kRowsK1b; ++j) v[j] = group_sum_last(v[j], d.lanes);
-#pragma unroll
-  for (int j = 0; j < kRowsK1b; ++j)
-    if (g0 + j < ngroups && d.col == d.lanes - 1) L.y_shared[(g0 + j) * d.rpw + d.rig] = v[j];
-}
-
-// K2: routed gate/up of the k selected experts.
-template <int BPLH>
-__global__ __launch_bounds__(kBlock) void k2_gateup(LayerT1 L, const uint16_t* __restrict__ x,
-                                                    const int32_t* __restrict__ idx,
-                                                    float* __restrict__ act, int gu_lanes) {
-  __shared__ __align__(16) uint32_t x_lds[kMaxH / 2];
-  __shared__ int32_t e_lds[kMaxTopK];
-  const int wid = wave_id();
-  if (threadIdx.x < L.k) {
-    const int e = idx[threadIdx.x];
-    e_lds[threadIdx.x] = e < 0 ? 0 : (e >= L.E ? L.E - 1 : e);  // never address outside
-  }
-  stage_x(x, nullptr, 0.f, L.H, x_lds, nullptr, nullptr);
   GateUp<BPLH> g;
   g.init(gu_lanes, L.F);
   const GateUpJob J{L.g_codes, L.g_scales, L.u_codes, L.u_scales, e_lds, L.H, L.F, act};
-  gateup_tasks(g, J, x_lds, L.k * g.tps, blockIdx.x * kWaves + wid, gridDim.x * kWaves);
+  const int first = gb * kWaves + wid, ntask = L.k * g.tps;
+  uint4 ca[BPLH];
+  uint32_t sa[BPLH];
+  g.load(J, first < ntask ? first : ntask - 1, ca, sa);
+  stage_x_store(xs, L.H, x_lds);
+  if (!idx && gb == 0 && threadIdx.x < L.k) {
+    const int e = e_lds[threadIdx.x];
+    const float w = w_lds[threadIdx.x];
+    L.idx[threadIdx.x] = e;
+    L.wts[threadIdx.x] = w;
+    if (L.idx_out) L.idx_out[threadIdx.x] = e;
+    if (L.w_out) L.w_out[threadIdx.x] = w;
+  }
+  gateup_tasks(g, J, x_lds, ntask, first, (gridDim.x - n_sd) * kWaves, ca, sa);
 }
 
-// K3: one workgroup of kK3Waves waves per row slab of `gpb` row groups.  Wave
-// w streams the slab's rows of slots w, w + kK3Waves, ... (activations of the
-// slot held in registers) and adds each weighted row result to its own LDS
-// partial; the waves' partials are then added in wave order together with
-// the shared output and the residual.
+// K3: one workgroup of kK3Waves waves per row slab of `gpb` row groups, one
+// slab per CU.  Wave w streams the slab's rows of two slots at once, w and
+// w + kK3Waves (then w + 2 kK3Waves and w + 3 kK3Waves, ...), with the
+// activations of both slots in registers.  Rows go in bursts of kK3Burst row
+// groups per slot, double-buffered: the next burst is requested before the
+// current one is reduced, so every wave keeps one to two bursts in flight.
+// A wave without a second slot repeats the first with weight 0.  Each
+// weighted row result is added to the wave's own LDS partial; the partials
+// are then summed in wave order together with the shared output and the
+// residual.  Expert ids and weights are read by each wave directly (they are
+// wave-uniform), so the first weight requests wait for no barrier.  (F = 4096
+// keeps one slot per pass: its two blocks per lane double the activation
+// registers.)
 constexpr int kK3Waves = 8;
 constexpr int kK3Block = kK3Waves * kWave;
 constexpr int kK3MaxRows = 64;
-constexpr int kK3SlabsPerCU = 2;
-template <int BPLF>
+constexpr int kK3Burst = 4;
+
+template <int BPLF, int LANES>
+struct DownBurst {
+  uint4 ca[kK3Burst][BPLF], cb[kK3Burst][BPLF];
+  uint32_t xa[kK3Burst][BPLF], xb[kK3Burst][BPLF];
+};
+
+template <int BPLF, int LANES>
 __global__ __launch_bounds__(kK3Block) void k3_down_combine(LayerT1 L, int dn_lanes, int gpb) {
   __shared__ float red[kK3Waves][kK3MaxRows];
-  __shared__ int32_t e_lds[kMaxTopK];
-  __shared__ float w_lds[kMaxTopK];
-  constexpr int NB = 8 / BPLF;  // row groups per burst of loads
+  constexpr bool TWO = BPLF == 1;
+  constexpr int NB = kK3Burst;
   const int wid = wave_id(), lane = threadIdx.x & 63;
-  DownLanes<BPLF> d;
-  d.init_map(dn_lanes);
-  const int ngroups = L.H / d.rpw;
+  DownLanes<BPLF, LANES> dA, dB;
+  dA.init_map(dn_lanes);
+  dB.init_map(dn_lanes);
+  const int ngroups = L.H / dA.rpw;
   const int gbase = blockIdx.x * gpb;
   const int ng = ngroups - gbase < gpb ? ngroups - gbase : gpb;  // groups of this slab
-  const int R = ng * d.rpw;
+  const int R = ng * dA.rpw;
+  // each wave zeroes and later accumulates only its own partial row: no
+  // barrier needed before the first accumulation
   for (int t = lane; t < R; t += kWave) red[wid][t] = 0.f;
-  if (threadIdx.x < L.k) {
-    const int e = L.idx[threadIdx.x];
-    e_lds[threadIdx.x] = e < 0 ? 0 : (e >= L.E ? L.E - 1 : e);
-    w_lds[threadIdx.x] = L.wts[threadIdx.x];
-  }
-  __syncthreads();
+  // shared output and residual of this thread's output row, requested now
+  // so that the final combine waits on nothing but LDS.  Raw 32-bit buffer
+  // reads: an absent operand gets a zero-sized descriptor and reads as 0,
+  // and nothing branches on it.
+  const int trow = gbase * dA.rpw + (threadIdx.x < R ? threadIdx.x : 0);
+  const uint32_t ys_bits =
+      buf_ld4(buf_rsrc(L.y_shared, L.S ? (uint32_t)L.H * 4u : 0u), (uint32_t)trow * 4u, 0u);
+  const uint32_t res_word = buf_ld4(buf_rsrc(L.residual, L.residual ? (uint32_t)L.H * 2u : 0u),
+                                    ((uint32_t)trow * 2u) & ~3u, 0u);
 
-  for (int s = wid; s < L.k; s += kK3Waves) {
-    const int e = e_lds[s];
-    const float w = w_lds[s];
-    const uint8_t* codes = L.d_codes + (size_t)e * L.H * (L.F / 2);
-    const uint8_t* scales = L.d_scales + (size_t)e * L.H * (L.F / 32);
-    d.load_act(L.act + (size_t)s * L.F);
-    for (int g0 = 0; g0 < ng; g0 += NB) {
-      uint4 c[NB][BPLF];
-      uint32_t sc[NB][BPLF];
+  const size_t mat_c = (size_t)L.H * (L.F / 2), mat_s = (size_t)L.H * (L.F / 32);
+  const int step = TWO ? 2 * kK3Waves : kK3Waves;
+  for (int s0 = wid; s0 < L.k; s0 += step) {
+    const int sb = s0 + kK3Waves;
+    const bool hasB = TWO && sb < L.k;
+    const int sB = hasB ? sb : s0;
+    // uniform values: make them scalar so the row bases stay in SGPRs
+    const int e0 = __builtin_amdgcn_readfirstlane(L.idx[s0]);
+    const int e1 = __builtin_amdgcn_readfirstlane(L.idx[sB]);
+    const int eA = e0 < 0 ? 0 : (e0 >= L.E ? L.E - 1 : e0);  // never address outside
+    const int eB = e1 < 0 ? 0 : (e1 >= L.E ? L.E - 1 : e1);
+    const auto rcA = buf_rsrc(L.d_codes + eA * mat_c, (uint32_t)mat_c);
+    const auto rsA = buf_rsrc(L.d_scales + eA * mat_s, (uint32_t)mat_s);
+    const auto rcB = buf_rsrc(L.d_codes + eB * mat_c, (uint32_t)mat_c);
+    const auto rsB = buf_rsrc(L.d_scales + eB * mat_s, (uint32_t)mat_s);
+    auto load_burst = [&](int g0, DownBurst<BPLF, LANES>& P) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int g = g0 + j < ng ? g0 + j : ng - 1;
-        d.load_row(codes, scales, L.F, (gbase + g) * d.rpw + d.rig, c[j], sc[j]);
+        const int row0 = (gbase + (g0 + j < ng ? g0 + j : ng - 1)) * dA.rpw;
+        dA.load_row_buf(rcA, rsA, L.F, row0, P.ca[j], P.xa[j]);
+        if (TWO) dB.load_row_buf(rcB, rsB, L.F, row0, P.cb[j], P.xb[j]);
       }
+    };
+    DownBurst<BPLF, LANES> P, Q;
+    load_burst(0, P);
+    const float wA = L.wts[s0], wB = hasB ? L.wts[sB] : 0.f;
+    dA.load_act(L.act + (size_t)s0 * L.F);
+    if (TWO) dB.load_act(L.act + (size_t)sB * L.F);
+    auto use_burst = [&](int g0, const DownBurst<BPLF, LANES>& P) {
       float v[NB];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) v[j] = d.dot(c[j], sc[j]);
+      for (int j = 0; j < NB; ++j) {
+        // one row of one slot at a time: unpacking more at once costs registers
+        v[j] = wA * dA.dot(P.ca[j], P.xa[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (TWO) v[j] = __builtin_fmaf(wB, dB.dot(P.cb[j], P.xb[j]), v[j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-      for (int j = 0; j < NB; ++j) v[j] = group_sum_last(v[j], d.lanes);
+      for (int j = 0; j < NB; ++j) v[j] = dA.reduce(v[j]);
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        if (g0 + j < ng && d.col == d.lanes - 1) red[wid][(g0 + j) * d.rpw + d.rig] += w * v[j];
+        if (g0 + j < ng && dA.col == dA.lanes - 1) red[wid][(g0 + j) * dA.rpw + dA.rig] += v[j];
+    };
+    // Every request is unconditional (the burst index is clamped): a load
+    // under a branch that rejoins makes the compiler wait for the newer
+    // loads as well.  The one redundant burst per pass re-reads rows this
+    // wave has just requested, so it is served by L2.
+    const int nb = (ng + NB - 1) / NB;
+    for (int i = 0; i < nb; i += 2) {
+      load_burst((i + 1 < nb ? i + 1 : nb - 1) * NB, Q);
+      __builtin_amdgcn_sched_barrier(0);
+      use_burst(i * NB, P);
+      if (i + 1 >= nb) break;
+      load_burst((i + 2 < nb ? i + 2 : nb - 1) * NB, P);
+      __builtin_amdgcn_sched_barrier(0);
+      use_burst((i + 1) * NB, Q);
     }
   }
   __syncthreads();
   const int nwk = L.k < kK3Waves ? L.k : kK3Waves;
-  for (int t = threadIdx.x; t < R; t += kK3Block) {
+  if ((int)threadIdx.x < R) {  // R <= kK3MaxRows < kK3Block
     float tot = 0.f;
-    for (int v = 0; v < nwk; ++v) tot += red[v][t];
-    const int row = gbase * d.rpw + t;
-    if (L.S) tot += L.y_shared[row];
-    if (L.residual) tot += bf16_to_f32(L.residual[row]);
-    const uint16_t o = f32_to_bf16(tot);
-    L.out[row] = o;
-    if (L.trace) L.trace[row] = o;
+    for (int v = 0; v < nwk; ++v) tot += red[v][threadIdx.x];
+    const float tail = __uint_as_float(ys_bits) + bf16_to_f32((res_word >> (16 * (trow & 1))) & 0xFFFFu);
+    const uint16_t o = f32_to_bf16(tot + tail);
+    L.out[trow] = o;
+    if (L.trace) L.trace[trow] = o;
   }
 }
 
@@ -460,8 +638,15 @@ hipError_t k1a_launch(const LayerT1& L, int n_router, int n_shared, int lanes, h
 
 template <int B>
 hipError_t k2_launch(const LayerT1& L, const uint16_t* x, const int32_t* idx, float* act,
-                     int n_gu, int lanes, hipStream_t s) {
-  hipLaunchKernelGGL(k2_gateup<B>, dim3(n_gu), dim3(kBlock), 0, s, L, x, idx, act, lanes);
+                     int n_gu, int lanes, int n_sd, const RowMap& dm, hipStream_t s) {
+  if (dm.bpl == 1)
+    hipLaunchKernelGGL((k2_gateup<B, 1>), dim3(n_sd + n_gu), dim3(kBlock), 0, s, L, x, idx, act,
+                       lanes, n_sd, dm.lanes);
+  else if (dm.bpl == 2)
+    hipLaunchKernelGGL((k2_gateup<B, 2>), dim3(n_sd + n_gu), dim3(kBlock), 0, s, L, x, idx, act,
+                       lanes, n_sd, dm.lanes);
+  else
+    return hipErrorInvalidValue;
   return hipPeekAtLastError();
 }
 
@@ -488,34 +673,27 @@ hipError_t launch_router_t1(const LayerT1& L, bool with_shared, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_topk_t1(const LayerT1& L, bool with_shared, hipStream_t s) {
-  const RowMap dm = down_map(L.F);
-  int n_sd = 0;
-  if (with_shared && L.S) n_sd = ceil_div(L.H / (kWave / dm.lanes), kWaves * kRowsK1b);
-  if (dm.bpl == 1)
-    hipLaunchKernelGGL(k1_topk<1>, dim3(1 + n_sd), dim3(kBlock), 0, s, L, dm.lanes);
-  else if (dm.bpl == 2)
-    hipLaunchKernelGGL(k1_topk<2>, dim3(1 + n_sd), dim3(kBlock), 0, s, L, dm.lanes);
-  else
-    return hipErrorInvalidValue;
+hipError_t launch_topk_t1(const LayerT1& L, hipStream_t s) {
+  hipLaunchKernelGGL(k1_topk, dim3(1), dim3(kBlock), 0, s, L);
   return hipPeekAtLastError();
 }
 
 hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* idx, float* act,
-                            hipStream_t s) {
-  const RowMap gm = gateup_map(L.H);
+                            bool with_shared_down, hipStream_t s) {
+  const RowMap gm = gateup_map(L.H), dm = down_map(L.F);
   const int tasks = L.k * (L.F / (32 / gm.lanes));
   const int cap = kNumCU * kK2WavesPerCU / kWaves;
   const int n_gu = ceil_div(tasks, kWaves * 4) < cap ? ceil_div(tasks, kWaves * 4) : cap;
+  const int n_sd = (with_shared_down && L.S) ? ceil_div(L.H / (kWave / dm.lanes), kWaves * kRowsSd) : 0;
   switch (gm.bpl) {
-    case 1: return k2_launch<1>(L, x, idx, act, n_gu, gm.lanes, s);
-    case 2: return k2_launch<2>(L, x, idx, act, n_gu, gm.lanes, s);
-    case 3: return k2_launch<3>(L, x, idx, act, n_gu, gm.lanes, s);
-    case 4: return k2_launch<4>(L, x, idx, act, n_gu, gm.lanes, s);
-    case 5: return k2_launch<5>(L, x, idx, act, n_gu, gm.lanes, s);
-    case 6: return k2_launch<6>(L, x, idx, act, n_gu, gm.lanes, s);
-    case 7: return k2_launch<7>(L, x, idx, act, n_gu, gm.lanes, s);
-    case 8: return k2_launch<8>(L, x, idx, act, n_gu, gm.lanes, s);
+    case 1: return k2_launch<1>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
+    case 2: return k2_launch<2>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
+    case 3: return k2_launch<3>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
+    case 4: return k2_launch<4>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
+    case 5: return k2_launch<5>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
+    case 6: return k2_launch<6>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
+    case 7: return k2_launch<7>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
+    case 8: return k2_launch<8>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
   }
   return hipErrorInvalidValue;
 }
@@ -523,15 +701,21 @@ hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* 
 hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s) {
   const RowMap dm = down_map(L.F);
   const int ngroups = L.H / (kWave / dm.lanes);
-  const int gpb = ceil_div(ngroups, kNumCU * kK3SlabsPerCU);
+  const int gpb = ceil_div(ngroups, kNumCU);  // one slab per CU
   const int nblk = ceil_div(ngroups, gpb);
   if (gpb * (kWave / dm.lanes) > kK3MaxRows) return hipErrorInvalidValue;
-  if (dm.bpl == 1)
-    hipLaunchKernelGGL(k3_down_combine<1>, dim3(nblk), dim3(kK3Block), 0, s, L, dm.lanes, gpb);
-  else if (dm.bpl == 2)
-    hipLaunchKernelGGL(k3_down_combine<2>, dim3(nblk), dim3(kK3Block), 0, s, L, dm.lanes, gpb);
-  else
-    return hipErrorInvalidValue;
+  // one expert's down matrix is addressed through a 32-bit buffer descriptor
+  if ((size_t)L.H * (size_t)(L.F / 2) > 0x7FFFFFFFu) return hipErrorInvalidValue;
+  const dim3 g(nblk), b(kK3Block);
+#define K3(BP, LN) hipLaunchKernelGGL((k3_down_combine<BP, LN>), g, b, 0, s, L, dm.lanes, gpb)
+  if (dm.bpl == 2) K3(2, 64);
+  else if (dm.lanes == 64) K3(1, 64);
+  else if (dm.lanes == 32) K3(1, 32);
+  else if (dm.lanes == 16) K3(1, 16);
+  else if (dm.lanes == 8) K3(1, 8);
+  else if (dm.lanes == 4) K3(1, 4);
+  else return hipErrorInvalidValue;
+#undef K3
   return hipPeekAtLastError();
 }
 
