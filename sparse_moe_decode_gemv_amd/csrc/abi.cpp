@@ -27,7 +27,7 @@ struct Carver {
 
 // Single-token layout.
 struct WsT1 {
-  size_t reserved, logits, idx, wts, act, y_shared, xn, total;
+  size_t reserved, logits, idx, wts, act, xn, total;
 };
 
 WsT1 ws_t1(const moe_shape& s) {
@@ -39,7 +39,6 @@ WsT1 ws_t1(const moe_shape& s) {
   L.idx = c.take(sizeof(int32_t) * s.top_k);
   L.wts = c.take(sizeof(float) * s.top_k);
   L.act = c.take(sizeof(float) * nslot * s.ffn);
-  L.y_shared = c.take(sizeof(float) * s.hidden);
   L.xn = c.take(sizeof(uint16_t) * s.hidden);
   L.total = c.o;
   return L;
@@ -176,7 +175,6 @@ LayerT1 make_layer(const moe_shape* s, const moe_layer_weights* w, void* ws) {
   L.idx = (int32_t*)(b + W.idx);
   L.wts = (float*)(b + W.wts);
   L.act = (float*)(b + W.act);
-  L.y_shared = (float*)(b + W.y_shared);
   L.xn = (uint16_t*)(b + W.xn);
   return L;
 }
@@ -214,10 +212,10 @@ LayerTB make_layer_tb(const moe_shape* s, const moe_layer_weights* w, void* ws, 
 
 uint16_t* xn_tb(const moe_shape* s, void* ws, int T) { return (uint16_t*)((char*)ws + ws_tb(*s, T).xn); }
 
-// One full single-token layer: K1a (router + shared gate/up), K2 (top-k,
-// routed gate/up, shared down), K3 (down + combine) on one stream.
+// One full single-token layer: K1a (router), K2 (top-k, shared + routed
+// gate/up), K3 (down of every slot + combine) on one stream.
 int run_layer_t1(LayerT1& L, hipStream_t st) {
-  hipError_t e = moe::launch_router_t1(L, true, st);
+  hipError_t e = moe::launch_router_t1(L, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const uint16_t* xin = L.gamma ? L.xn : L.x;
   e = moe::launch_gateup_t1(L, xin, nullptr, L.act, true, st);
@@ -285,7 +283,7 @@ int moe_router_topk(const moe_shape* shape, const uint16_t* x, const uint16_t* r
     L.idx_out = topk_idx;
     L.w_out = topk_w;
     L.logits_out = logits;
-    if (moe::launch_router_t1(L, false, st) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_router_t1(L, st) != hipSuccess) return MOE_ERR_HIP;
     return hip_status(moe::launch_topk_t1(L, st));
   }
   LayerTB L = make_layer_tb(shape, nullptr, ws, n_tokens);

@@ -54,7 +54,6 @@ struct LayerT1 {
   int32_t* idx;        // [k]
   float* wts;          // [k]
   float* act;          // [k + S][F]: routed slots, then the shared expert
-  float* y_shared;     // [H] shared expert output
   uint16_t* xn;        // [H] normalised input (stack)
   // optional user outputs
   float* logits_out;
@@ -62,14 +61,13 @@ struct LayerT1 {
   float* w_out;
 };
 
-// K1a router (+ shared gate/up), K2 top-k when idx is null (+ shared down
-// when asked) and gate/up, K3 down + combine; launch_topk_t1 is the
-// stand-alone top-k of the router entry point.  with_shared = false skips
-// the shared-expert work.
-hipError_t launch_router_t1(const LayerT1& L, bool with_shared, hipStream_t s);
+// K1a router, K2 top-k when idx is null and gate/up (shared expert first
+// when with_shared), K3 down of every slot (the shared expert last) +
+// combine; launch_topk_t1 is the stand-alone top-k of the router entry point.
+hipError_t launch_router_t1(const LayerT1& L, hipStream_t s);
 hipError_t launch_topk_t1(const LayerT1& L, hipStream_t s);
 hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* idx,
-                            float* act, bool with_shared_down, hipStream_t s);
+                            float* act, bool with_shared, hipStream_t s);
 hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s);
 
 // ---- 2 <= T <= 64 path ------------------------------------------------------

@@ -1,20 +1,20 @@
 // Single-token (batch 1) decode layer: three kernels per layer, one stream.
 //
 //  K1a router GEMV over all E rows (one wave per row, every load of the row
-//      in flight at once).  Spare workgroups stream the shared expert's
-//      gate/up rows: the shared expert does not depend on routing (the pages
-//      run it beside the selected experts: page "AI手搓1.2万行代码榨干GB300!…",
-//      section 02; smzdm page, section "四步改造").
-//  K2  top-k + softmax (radix select) in every gate/up workgroup, then the
-//      gate/up GEMVs of the k selected experts with fused MXFP4 dequant and
-//      SiLU gating -> fp32 activations; the first workgroups run the shared
-//      expert's down projection meanwhile, so the selection latency is spent
-//      under shared-expert bytes.
-//  K3  down GEMVs of the selected experts, router-weighted combine with the
-//      shared output (weight 1) and residual add -> bf16.  One 16-wave
-//      workgroup per CU owns a slab of output rows, wave w streams slot w's
-//      rows of the slab, and the slots are summed in LDS in a fixed order
-//      (deterministic, no floating-point atomics).
+//      in flight at once).
+//  K2  top-k + softmax (radix select) in every workgroup, then gate/up GEMVs
+//      with fused MXFP4 dequant and SiLU gating -> fp32 activations: first
+//      the shared expert's rows, then those of the k selected experts.  The
+//      shared expert does not depend on routing (the pages run it beside the
+//      selected experts: page "AI手搓1.2万行代码榨干GB300!…", section 02;
+//      smzdm page, section "四步改造"), so every wave requests its shared
+//      rows before the selection and the selection latency is spent under
+//      shared-expert bytes.
+//  K3  down GEMVs of the k selected experts and of the shared expert,
+//      router-weighted combine (shared weight 1) and residual add -> bf16.
+//      One workgroup per CU owns a slab of output rows, each wave streams
+//      two slots' rows of the slab, and the slots are summed in LDS in a
+//      fixed order (deterministic, no floating-point atomics).
 //
 // Decode is bound by streaming weights from HBM (page "英伟达用1.2万行CuTe DSL
 // Megakernel…", section "解码优化为何比训练优化更难"; tmtpost page, section
@@ -194,36 +194,58 @@ __device__ __forceinline__ void router_row_finish(const LayerT1& L, int e, const
 // Gate/up row pairs.  Lanes 0..31 stream gate rows, lanes 32..63 the up rows
 // with the same index; `lanes` lanes per row (8, 16 or 32), BPL blocks per
 // lane, 32/lanes rows per half wave.  A task is one such group of row pairs.
-// x comes from LDS, so the registers hold only weights in flight: every
-// wave keeps two tasks' loads outstanding (static double buffer).
+// Tasks 0 .. ns-1 belong to the shared expert (no routing needed, so they
+// can be requested before the selection is known), tasks ns .. are the
+// routed slots in order.  x comes from LDS, so the registers hold only
+// weights in flight: every wave keeps two tasks' loads outstanding.
 struct GateUpJob {
-  const uint8_t *g_codes, *g_scales, *u_codes, *u_scales;
-  const int32_t* e_lds;  // expert of each slot, in LDS (null: expert 0)
-  int H, F;
-  float* act;            // [slots][F]
+  const uint8_t *g_codes, *g_scales, *u_codes, *u_scales;      // routed [E][F][H]
+  const uint8_t *sg_codes, *sg_scales, *su_codes, *su_scales;  // shared [F][H]
+  const int32_t* e_lds;  // expert of each routed slot, in LDS
+  int H, F, k;
+  int ns;                // shared tasks (0 without a shared expert)
+  float* act;            // [k + 1][F]: routed slots, then the shared expert
 };
 
 template <int BPL>
 struct GateUp {
   int half, rig, col, lanes, rph, tps;
+  // this lane's matrices (gate for lanes 0..31, up for 32..63), routed and
+  // shared: chosen once, so that a task only selects between the two
+  const uint8_t *rc, *rs, *shc, *shs;
 
-  __device__ void init(int lanes_, int F) {
+  __device__ void init(const GateUpJob& J, int lanes_) {
     const int lane = threadIdx.x & 63;
     lanes = lanes_;
     half = lane >> 5;
     rig = (lane & 31) / lanes;
     col = (lane & 31) % lanes;
     rph = 32 / lanes;
-    tps = F / rph;
+    tps = J.F / rph;
+    rc = half ? J.u_codes : J.g_codes;
+    rs = half ? J.u_scales : J.g_scales;
+    shc = half ? J.su_codes : J.sg_codes;
+    shs = half ? J.su_scales : J.sg_scales;
+  }
+  // act row (slot; k for the shared expert) and matrix row of task t
+  __device__ __forceinline__ void locate(const GateUpJob& J, int t, bool& sh, int& slot,
+                                         int& j) const {
+    sh = t < J.ns;
+    const int tr = sh ? t : t - J.ns;
+    const int s = sh ? 0 : tr / tps;
+    slot = sh ? J.k : s;
+    j = (tr - s * tps) * rph + rig;
   }
   __device__ __forceinline__ void load(const GateUpJob& J, int t, uint4 (&c)[BPL],
                                        uint32_t (&sc)[BPL]) const {
-    const int s = t / tps;
-    const int j = (t - s * tps) * rph + rig;
-    const int e = J.e_lds ? J.e_lds[s] : 0;
-    const size_t row = (size_t)e * J.F + j;
-    const uint8_t* cb = (half ? J.u_codes : J.g_codes) + row * (size_t)(J.H / 2);
-    const uint8_t* sb = (half ? J.u_scales : J.g_scales) + row * (size_t)(J.H / 32);
+    bool sh;
+    int slot, j;
+    locate(J, t, sh, slot, j);
+    // selects, not branches: the loads stay unconditional
+    const int e = J.e_lds[sh ? 0 : slot];
+    const size_t row = (size_t)(sh ? 0 : e) * J.F + j;
+    const uint8_t* cb = (sh ? shc : rc) + row * (size_t)(J.H / 2);
+    const uint8_t* sb = (sh ? shs : rs) + row * (size_t)(J.H / 32);
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
       const int b = col + lanes * i;
@@ -249,16 +271,16 @@ struct GateUp {
       // rows are 4-byte multiples and lanes % 4 == 0: block b's byte is b & 3
       const float scale = e8m0_to_f32(byte_of(sc[i], (col + lanes * i) & 3));
       acc = __builtin_fmaf(block_dot_bf16(c[i], xv), scale, acc);
-      // keep the x reads of later blocks from being hoisted: shorter live
-      // ranges give three waves per SIMD instead of two
+      // keep the x reads of later blocks from being hoisted (register use)
       __builtin_amdgcn_sched_barrier(0);
     }
     acc = group_sum_last(acc, lanes);
     const float up = __shfl_xor(acc, 32, kWave);
     if (half == 0 && col == lanes - 1) {
-      const int s = t / tps;
-      const int j = (t - s * tps) * rph + rig;
-      J.act[(size_t)s * J.F + j] = silu(acc) * up;
+      bool sh;
+      int slot, j;
+      locate(J, t, sh, slot, j);
+      J.act[(size_t)slot * J.F + j] = silu(acc) * up;
     }
   }
 };
@@ -371,64 +393,22 @@ struct DownLanes {
 };
 
 // -------------------------------------------------------------------------
-// K1a: router rows (+ shared gate/up in the workgroups past n_router).  Each
-// wave requests its first weights before x is staged (RMSNorm'ed for the
-// stack), so that the weight stream starts at once.
-template <int BPLH>
-__global__ __launch_bounds__(kBlock) void k1_router(LayerT1 L, int n_router, int gu_lanes) {
+// K1a: router rows.  Each wave requests its first row before x is staged
+// (RMSNorm'ed for the stack; workgroup 0 also stores the normalised x for
+// the next kernel), so that the weight stream starts at once.
+__global__ __launch_bounds__(kBlock) void k1_router(LayerT1 L) {
   __shared__ __align__(16) uint32_t x_lds[kMaxH / 2];
   __shared__ float red[kWaves];
   const int wid = wave_id();
-  if ((int)blockIdx.x < n_router) {
-    const int gw = blockIdx.x * kWaves + wid, nw = n_router * kWaves;
-    RouterRow R;
-    const int e0 = gw < L.E ? gw : L.E - 1;
-    router_row_load(L, e0, R);
-    stage_x(L.x, L.gamma, L.eps, L.H, x_lds, red, (L.gamma && blockIdx.x == 0) ? L.xn : nullptr);
-    if (gw < L.E) router_row_finish(L, gw, R, x_lds);
-    for (int e = gw + nw; e < L.E; e += nw) {
-      router_row_load(L, e, R);
-      router_row_finish(L, e, R, x_lds);
-    }
-    return;
+  const int gw = blockIdx.x * kWaves + wid, nw = gridDim.x * kWaves;
+  RouterRow R;
+  router_row_load(L, gw < L.E ? gw : L.E - 1, R);
+  stage_x(L.x, L.gamma, L.eps, L.H, x_lds, red, (L.gamma && blockIdx.x == 0) ? L.xn : nullptr);
+  if (gw < L.E) router_row_finish(L, gw, R, x_lds);
+  for (int e = gw + nw; e < L.E; e += nw) {
+    router_row_load(L, e, R);
+    router_row_finish(L, e, R, x_lds);
   }
-  GateUp<BPLH> g;
-  g.init(gu_lanes, L.F);
-  const GateUpJob J{L.sg_codes, L.sg_scales, L.su_codes, L.su_scales, nullptr, L.H, L.F,
-                    L.act + (size_t)L.k * L.F};
-  const int first = (blockIdx.x - n_router) * kWaves + wid;
-  uint4 ca[BPLH];
-  uint32_t sa[BPLH];
-  g.load(J, first < g.tps ? first : g.tps - 1, ca, sa);
-  stage_x(L.x, L.gamma, L.eps, L.H, x_lds, red, nullptr);
-  gateup_tasks(g, J, x_lds, g.tps, first, (gridDim.x - n_router) * kWaves, ca, sa);
-}
-
-// Shared expert's down rows -> y_shared: wave gw takes kRowsSd row groups
-// with all their loads in flight.
-constexpr int kRowsSd = 8;
-template <int BPLF>
-__device__ void shared_down_rows(const LayerT1& L, int dn_lanes, int gw) {
-  DownLanes<BPLF> d;
-  d.init_map(dn_lanes);
-  d.load_act(L.act + (size_t)L.k * L.F);
-  const int ngroups = L.H / d.rpw;
-  const int g0 = gw * kRowsSd;
-  uint4 c[kRowsSd][BPLF];
-  uint32_t sc[kRowsSd][BPLF];
-#pragma unroll
-  for (int j = 0; j < kRowsSd; ++j) {
-    const int g = g0 + j < ngroups ? g0 + j : ngroups - 1;
-    d.load_row(L.sd_codes, L.sd_scales, L.F, g * d.rpw, c[j], sc[j]);
-  }
-  float v[kRowsSd];
-#pragma unroll
-  for (int j = 0; j < kRowsSd; ++j) v[j] = d.dot(c[j], sc[j]);
-#pragma unroll
-  for (int j = 0; j < kRowsSd; ++j) v[j] = group_sum_last(v[j], d.lanes);
-#pragma unroll
-  for (int j = 0; j < kRowsSd; ++j)
-    if (g0 + j < ngroups && d.col == d.lanes - 1) L.y_shared[(g0 + j) * d.rpw + d.rig] = v[j];
 }
 
 // K1b (router-only entry point): top-k + softmax of the logits, one workgroup.
@@ -443,55 +423,58 @@ __global__ __launch_bounds__(kBlock) void k1_topk(LayerT1 L) {
   topk_softmax_block(lg, L.E, L.k, tk, L.idx, L.wts, L.idx_out, L.w_out);
 }
 
-// K2: routed gate/up of the k selected experts.  With idx == null the
-// experts are selected here: every gate/up workgroup runs the same top-k on
-// the router logits (deterministic, identical in every workgroup) and
-// workgroup n_sd publishes the indices and weights for K3 and the caller.
-// The first n_sd workgroups instead run the shared expert's down rows
-// (shared activations from K1a) -> y_shared: they need no routing, so they
-// are placed first and stream while the others select.
-template <int BPLH, int BPLF>
+// K2: gate/up of the shared expert and of the k selected experts.  With
+// idx == null the experts are selected here: every workgroup runs the same
+// top-k on the router logits (deterministic, identical in every workgroup)
+// and workgroup 0 publishes the indices and weights for K3 and the caller.
+// PRE (a shared expert, and no more waves than shared tasks): every wave's
+// first task is a shared one, requested before the selection, so the
+// selection latency is spent under shared-expert bytes.
+template <int BPLH, bool PRE>
 __global__ __launch_bounds__(kBlock) void k2_gateup(LayerT1 L, const uint16_t* __restrict__ x,
                                                     const int32_t* __restrict__ idx,
-                                                    float* __restrict__ act, int gu_lanes, int n_sd,
-                                                    int dn_lanes) {
+                                                    float* __restrict__ act, int gu_lanes, int ns) {
   __shared__ __align__(16) uint32_t x_lds[kMaxH / 2];
   __shared__ int32_t e_lds[kMaxTopK];
   __shared__ float w_lds[kMaxTopK];
   __shared__ TopkLds tk;
   const int wid = wave_id();
-  if ((int)blockIdx.x < n_sd) {
-    shared_down_rows<BPLF>(L, dn_lanes, (int)blockIdx.x * kWaves + wid);
-    return;
-  }
-  const int gb = blockIdx.x - n_sd;
-  XStage xs;
-  stage_x_load(x, L.H, xs);
+  const GateUpJob J{L.g_codes,  L.g_scales,  L.u_codes,  L.u_scales, L.sg_codes, L.sg_scales,
+                    L.su_codes, L.su_scales, e_lds,      L.H,        L.F,        L.k,
+                    ns,         act};
+  GateUp<BPLH> g;
+  g.init(J, gu_lanes);
+  const int first = blockIdx.x * kWaves + wid, ntask = ns + L.k * g.tps;
+  // Request order matters: loads complete in order for the wait counter, so
+  // the selection's inputs go first and the shared weights last; waiting
+  // for the logits then leaves the shared weights in flight.
+  float lg[kTopkPerThread];
+  int32_t e_in = 0;
   if (idx) {
-    if (threadIdx.x < L.k) {
-      const int e = idx[threadIdx.x];
-      e_lds[threadIdx.x] = e < 0 ? 0 : (e >= L.E ? L.E - 1 : e);  // never address outside
-    }
-    __syncthreads();
+    e_in = idx[threadIdx.x < L.k ? threadIdx.x : 0];
   } else {
-    float lg[kTopkPerThread];
 #pragma unroll
     for (int i = 0; i < kTopkPerThread; ++i) {
       const int e = threadIdx.x * kTopkPerThread + i;
       lg[i] = L.logits[e < L.E ? e : L.E - 1];
     }
+  }
+  XStage xs;
+  stage_x_load(x, L.H, xs);
+  uint4 ca[BPLH];
+  uint32_t sa[BPLH];
+  if constexpr (PRE) g.load(J, first, ca, sa);  // first < ns: a shared task
+  if (idx) {
+    if (threadIdx.x < L.k)
+      e_lds[threadIdx.x] = e_in < 0 ? 0 : (e_in >= L.E ? L.E - 1 : e_in);  // never address outside
+    __syncthreads();
+  } else {
     topk_softmax_block(lg, L.E, L.k, tk, e_lds, w_lds, nullptr, nullptr);
     __syncthreads();
   }
-  GateUp<BPLH> g;
-  g.init(gu_lanes, L.F);
-  const GateUpJob J{L.g_codes, L.g_scales, L.u_codes, L.u_scales, e_lds, L.H, L.F, act};
-  const int first = gb * kWaves + wid, ntask = L.k * g.tps;
-  uint4 ca[BPLH];
-  uint32_t sa[BPLH];
-  g.load(J, first < ntask ? first : ntask - 1, ca, sa);
+  if constexpr (!PRE) g.load(J, first < ntask ? first : ntask - 1, ca, sa);
   stage_x_store(xs, L.H, x_lds);
-  if (!idx && gb == 0 && threadIdx.x < L.k) {
+  if (!idx && blockIdx.x == 0 && threadIdx.x < L.k) {
     const int e = e_lds[threadIdx.x];
     const float w = w_lds[threadIdx.x];
     L.idx[threadIdx.x] = e;
@@ -499,26 +482,27 @@ __global__ __launch_bounds__(kBlock) void k2_gateup(LayerT1 L, const uint16_t* _
     if (L.idx_out) L.idx_out[threadIdx.x] = e;
     if (L.w_out) L.w_out[threadIdx.x] = w;
   }
-  gateup_tasks(g, J, x_lds, ntask, first, (gridDim.x - n_sd) * kWaves, ca, sa);
+  gateup_tasks(g, J, x_lds, ntask, first, gridDim.x * kWaves, ca, sa);
 }
 
-// K3: one workgroup of kK3Waves waves per row slab of `gpb` row groups, one
-// slab per CU.  Wave w streams the slab's rows of two slots at once, w and
-// w + kK3Waves (then w + 2 kK3Waves and w + 3 kK3Waves, ...), with the
-// activations of both slots in registers.  Rows go in bursts of kK3Burst row
-// groups per slot, double-buffered: the next burst is requested before the
-// current one is reduced, so every wave keeps one to two bursts in flight.
-// A wave without a second slot repeats the first with weight 0.  Each
-// weighted row result is added to the wave's own LDS partial; the partials
-// are then summed in wave order together with the shared output and the
-// residual.  Expert ids and weights are read by each wave directly (they are
-// wave-uniform), so the first weight requests wait for no barrier.  (F = 4096
-// keeps one slot per pass: its two blocks per lane double the activation
-// registers.)
-constexpr int kK3Waves = 8;
-constexpr int kK3Block = kK3Waves * kWave;
+// K3: one workgroup per row slab of `gpb` row groups, one slab per CU.  With
+// nw waves, wave w streams the slab's rows of two routed slots at once, w
+// and w + nw (then w + 2 nw and w + 3 nw, ...), with the activations of
+// both slots in registers.  Rows go in bursts of kK3Burst row groups per
+// slot, double-buffered: the next burst is requested before the current one
+// is reduced, so every wave keeps one to two bursts in flight.  A wave left
+// with a single slot streams that slot alone.  The shared expert (weight 1)
+// is split by rows instead: wave w takes its share of the slab's rows.  Its
+// rows and activations need no routing, so they are requested first, while
+// the expert ids are still in flight, and reduced once the first routed
+// burst has been requested.  Each row result is added to the wave's own LDS
+// partial; the partials are then summed in wave order and the residual is
+// added.  (F = 4096 keeps one routed slot per pass: its two blocks per lane
+// double the activation registers.)
+constexpr int kK3MaxWaves = 8;  // 2 waves per SIMD: up to 256 registers
 constexpr int kK3MaxRows = 64;
 constexpr int kK3Burst = 4;
+constexpr int kK3ShRows = 4;     // shared row groups requested up front per wave
 
 template <int BPLF, int LANES>
 struct DownBurst {
@@ -526,15 +510,107 @@ struct DownBurst {
   uint32_t xa[kK3Burst][BPLF], xb[kK3Burst][BPLF];
 };
 
-template <int BPLF, int LANES>
-__global__ __launch_bounds__(kK3Block) void k3_down_combine(LayerT1 L, int dn_lanes, int gpb) {
-  __shared__ float red[kK3Waves][kK3MaxRows];
-  constexpr bool TWO = BPLF == 1;
+// Where a slot's down rows come from: buffer descriptors of its matrix, its
+// combine weight and its activations.
+struct DownSlot {
+  __amdgpu_buffer_rsrc_t rc, rs;
+  float w;
+  const float* act;
+};
+// Routed slot s (< k).  e_v / w_v hold the routed experts and weights one
+// per lane (lane i: slot i), loaded once by the caller, so that every slot
+// reads them with a lane read instead of a memory round trip of its own.
+__device__ __forceinline__ DownSlot routed_slot(const LayerT1& L, int s, int e_v, float w_v) {
+  const size_t mat_c = (size_t)L.H * (L.F / 2), mat_s = (size_t)L.H * (L.F / 32);
+  const int e0 = __builtin_amdgcn_readlane(e_v, s);
+  const int e = e0 < 0 ? 0 : (e0 >= L.E ? L.E - 1 : e0);  // never address outside
+  DownSlot d;
+  d.rc = buf_rsrc(L.d_codes + e * mat_c, (uint32_t)mat_c);
+  d.rs = buf_rsrc(L.d_scales + e * mat_s, (uint32_t)mat_s);
+  d.w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_v), s));
+  d.act = L.act + (size_t)s * L.F;
+  return d;
+}
+// The shared expert; without one the descriptors are empty (reads give 0)
+// and the activations point at slot 0 (in bounds, unused).
+__device__ __forceinline__ DownSlot shared_slot(const LayerT1& L) {
+  const size_t mat_c = (size_t)L.H * (L.F / 2), mat_s = (size_t)L.H * (L.F / 32);
+  DownSlot d;
+  d.rc = buf_rsrc(L.S ? L.sd_codes : nullptr, L.S ? (uint32_t)mat_c : 0u);
+  d.rs = buf_rsrc(L.S ? L.sd_scales : nullptr, L.S ? (uint32_t)mat_s : 0u);
+  d.w = 1.f;
+  d.act = L.act + (L.S ? (size_t)L.k * L.F : 0);
+  return d;
+}
+
+// One wave's pass over the slab for one or two routed slots (TWO),
+// accumulating into its LDS partial row `red`; `between` runs once the
+// first burst and the activations have been requested.  Every request is
+// unconditional (the burst index is clamped): a load under a branch that
+// rejoins makes the compiler wait for the newer loads as well.  The one
+// redundant burst per pass re-reads rows this wave has just requested, so
+// it is served by L2.
+template <int BPLF, int LANES, bool TWO, typename Between>
+__device__ __forceinline__ void down_pass(const LayerT1& L, const DownSlot& A, const DownSlot& B,
+                                          DownLanes<BPLF, LANES>& dA, DownLanes<BPLF, LANES>& dB,
+                                          int gbase, int ng, float* red, Between between) {
   constexpr int NB = kK3Burst;
+  auto load_burst = [&](int g0, DownBurst<BPLF, LANES>& P) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int row0 = (gbase + (g0 + j < ng ? g0 + j : ng - 1)) * dA.rpw;
+      dA.load_row_buf(A.rc, A.rs, L.F, row0, P.ca[j], P.xa[j]);
+      if (TWO) dB.load_row_buf(B.rc, B.rs, L.F, row0, P.cb[j], P.xb[j]);
+    }
+  };
+  DownBurst<BPLF, LANES> P, Q;
+  load_burst(0, P);
+  dA.load_act(A.act);
+  if (TWO) dB.load_act(B.act);
+  between();
+  auto use_burst = [&](int g0, const DownBurst<BPLF, LANES>& P) {
+    float v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      // one row of one slot at a time: unpacking more at once costs registers
+      v[j] = A.w * dA.dot(P.ca[j], P.xa[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (TWO) v[j] = __builtin_fmaf(B.w, dB.dot(P.cb[j], P.xb[j]), v[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) v[j] = dA.reduce(v[j]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (g0 + j < ng && dA.col == dA.lanes - 1) red[(g0 + j) * dA.rpw + dA.rig] += v[j];
+  };
+  const int nb = (ng + NB - 1) / NB;
+  for (int i = 0; i < nb; i += 2) {
+    load_burst((i + 1 < nb ? i + 1 : nb - 1) * NB, Q);
+    __builtin_amdgcn_sched_barrier(0);
+    use_burst(i * NB, P);
+    if (i + 1 >= nb) break;
+    load_burst((i + 2 < nb ? i + 2 : nb - 1) * NB, P);
+    __builtin_amdgcn_sched_barrier(0);
+    use_burst((i + 1) * NB, Q);
+  }
+}
+
+template <int BPLF, int LANES>
+__global__ __launch_bounds__(kK3MaxWaves * kWave) void k3_down_combine(LayerT1 L, int dn_lanes,
+                                                                       int gpb) {
+  __shared__ float red[kK3MaxWaves][kK3MaxRows];
+  constexpr bool PAIRS = BPLF == 1;
   const int wid = wave_id(), lane = threadIdx.x & 63;
-  DownLanes<BPLF, LANES> dA, dB;
+  const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
+  // routed experts and weights, lane i holding slot i (k <= 32 < 64); these
+  // go first so that waiting for them leaves the later requests in flight
+  const int e_v = L.idx[lane < L.k ? lane : 0];
+  const float w_v = L.wts[lane < L.k ? lane : 0];
+  DownLanes<BPLF, LANES> dA, dB, dS;
   dA.init_map(dn_lanes);
   dB.init_map(dn_lanes);
+  dS.init_map(dn_lanes);
   const int ngroups = L.H / dA.rpw;
   const int gbase = blockIdx.x * gpb;
   const int ng = ngroups - gbase < gpb ? ngroups - gbase : gpb;  // groups of this slab
@@ -542,82 +618,71 @@ __global__ __launch_bounds__(kK3Block) void k3_down_combine(LayerT1 L, int dn_la
   // each wave zeroes and later accumulates only its own partial row: no
   // barrier needed before the first accumulation
   for (int t = lane; t < R; t += kWave) red[wid][t] = 0.f;
-  // shared output and residual of this thread's output row, requested now
-  // so that the final combine waits on nothing but LDS.  Raw 32-bit buffer
-  // reads: an absent operand gets a zero-sized descriptor and reads as 0,
-  // and nothing branches on it.
+  // residual of this thread's output row, requested now so that the final
+  // combine waits on nothing but LDS.  A raw 32-bit buffer read: without a
+  // residual the descriptor is empty and the read gives 0, with no branch.
   const int trow = gbase * dA.rpw + (threadIdx.x < R ? threadIdx.x : 0);
-  const uint32_t ys_bits =
-      buf_ld4(buf_rsrc(L.y_shared, L.S ? (uint32_t)L.H * 4u : 0u), (uint32_t)trow * 4u, 0u);
   const uint32_t res_word = buf_ld4(buf_rsrc(L.residual, L.residual ? (uint32_t)L.H * 2u : 0u),
                                     ((uint32_t)trow * 2u) & ~3u, 0u);
-
-  const size_t mat_c = (size_t)L.H * (L.F / 2), mat_s = (size_t)L.H * (L.F / 32);
-  const int step = TWO ? 2 * kK3Waves : kK3Waves;
-  for (int s0 = wid; s0 < L.k; s0 += step) {
-    const int sb = s0 + kK3Waves;
-    const bool hasB = TWO && sb < L.k;
-    const int sB = hasB ? sb : s0;
-    // uniform values: make them scalar so the row bases stay in SGPRs
-    const int e0 = __builtin_amdgcn_readfirstlane(L.idx[s0]);
-    const int e1 = __builtin_amdgcn_readfirstlane(L.idx[sB]);
-    const int eA = e0 < 0 ? 0 : (e0 >= L.E ? L.E - 1 : e0);  // never address outside
-    const int eB = e1 < 0 ? 0 : (e1 >= L.E ? L.E - 1 : e1);
-    const auto rcA = buf_rsrc(L.d_codes + eA * mat_c, (uint32_t)mat_c);
-    const auto rsA = buf_rsrc(L.d_scales + eA * mat_s, (uint32_t)mat_s);
-    const auto rcB = buf_rsrc(L.d_codes + eB * mat_c, (uint32_t)mat_c);
-    const auto rsB = buf_rsrc(L.d_scales + eB * mat_s, (uint32_t)mat_s);
-    auto load_burst = [&](int g0, DownBurst<BPLF, LANES>& P) {
+  // this wave's share of the shared expert's row groups: [sh0, sh1)
+  const int sh0 = L.S ? wid * ng / nw : 0, sh1 = L.S ? (wid + 1) * ng / nw : 0;
+  const DownSlot SH = shared_slot(L);
+  uint4 shc[kK3ShRows][BPLF];
+  uint32_t shs[kK3ShRows][BPLF];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int row0 = (gbase + (g0 + j < ng ? g0 + j : ng - 1)) * dA.rpw;
-        dA.load_row_buf(rcA, rsA, L.F, row0, P.ca[j], P.xa[j]);
-        if (TWO) dB.load_row_buf(rcB, rsB, L.F, row0, P.cb[j], P.xb[j]);
-      }
-    };
-    DownBurst<BPLF, LANES> P, Q;
-    load_burst(0, P);
-    const float wA = L.wts[s0], wB = hasB ? L.wts[sB] : 0.f;
-    dA.load_act(L.act + (size_t)s0 * L.F);
-    if (TWO) dB.load_act(L.act + (size_t)sB * L.F);
-    auto use_burst = [&](int g0, const DownBurst<BPLF, LANES>& P) {
-      float v[NB];
+  for (int j = 0; j < kK3ShRows; ++j) {
+    const int g = sh0 + j < sh1 ? sh0 + j : (sh1 > sh0 ? sh1 - 1 : 0);
+    dS.load_row_buf(SH.rc, SH.rs, L.F, (gbase + g) * dS.rpw, shc[j], shs[j]);
+  }
+  dS.load_act(SH.act);
+  auto shared_rows = [&]() {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        // one row of one slot at a time: unpacking more at once costs registers
-        v[j] = wA * dA.dot(P.ca[j], P.xa[j]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (TWO) v[j] = __builtin_fmaf(wB, dB.dot(P.cb[j], P.xb[j]), v[j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) v[j] = dA.reduce(v[j]);
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        if (g0 + j < ng && dA.col == dA.lanes - 1) red[wid][(g0 + j) * dA.rpw + dA.rig] += v[j];
-    };
-    // Every request is unconditional (the burst index is clamped): a load
-    // under a branch that rejoins makes the compiler wait for the newer
-    // loads as well.  The one redundant burst per pass re-reads rows this
-    // wave has just requested, so it is served by L2.
-    const int nb = (ng + NB - 1) / NB;
-    for (int i = 0; i < nb; i += 2) {
-      load_burst((i + 1 < nb ? i + 1 : nb - 1) * NB, Q);
+    for (int j = 0; j < kK3ShRows; ++j) {
+      float v = dS.dot(shc[j], shs[j]);
       __builtin_amdgcn_sched_barrier(0);
-      use_burst(i * NB, P);
-      if (i + 1 >= nb) break;
-      load_burst((i + 2 < nb ? i + 2 : nb - 1) * NB, P);
-      __builtin_amdgcn_sched_barrier(0);
-      use_burst((i + 1) * NB, Q);
+      v = dS.reduce(v);
+      if (sh0 + j < sh1 && dS.col == dS.lanes - 1) red[wid][(sh0 + j) * dS.rpw + dS.rig] += v;
     }
+  };
+
+  const int step = PAIRS ? 2 * nw : nw;
+  auto routed = [&](int s0, auto between) {
+    const int sb = s0 + nw;
+    const DownSlot A = routed_slot(L, s0, e_v, w_v);
+    if (PAIRS && sb < L.k) {
+      const DownSlot B = routed_slot(L, sb, e_v, w_v);
+      down_pass<BPLF, LANES, PAIRS>(L, A, B, dA, dB, gbase, ng, red[wid], between);
+    } else {
+      down_pass<BPLF, LANES, false>(L, A, A, dA, dB, gbase, ng, red[wid], between);
+    }
+  };
+  // The first pass is not part of the loop: inside it the shared rows would
+  // be loop-invariant, and the compiler would reduce them (and wait for
+  // them) before the first routed burst is requested.
+  if (wid < L.k) {
+    routed(wid, [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      shared_rows();
+    });
+  } else {
+    shared_rows();  // a wave without routed slots
+  }
+  for (int s0 = wid + step; s0 < L.k; s0 += step) routed(s0, []() {});
+  // shared row groups past the ones requested up front (only when the slab
+  // has more than kK3ShRows groups per wave)
+  for (int g = sh0 + kK3ShRows; g < sh1; ++g) {
+    uint4 c[BPLF];
+    uint32_t x[BPLF];
+    dS.load_row_buf(SH.rc, SH.rs, L.F, (gbase + g) * dS.rpw, c, x);
+    const float v = dS.reduce(dS.dot(c, x));
+    if (dS.col == dS.lanes - 1) red[wid][g * dS.rpw + dS.rig] += v;
   }
   __syncthreads();
-  const int nwk = L.k < kK3Waves ? L.k : kK3Waves;
-  if ((int)threadIdx.x < R) {  // R <= kK3MaxRows < kK3Block
+  if ((int)threadIdx.x < R) {  // R <= kK3MaxRows <= the workgroup size
     float tot = 0.f;
-    for (int v = 0; v < nwk; ++v) tot += red[v][threadIdx.x];
-    const float tail = __uint_as_float(ys_bits) + bf16_to_f32((res_word >> (16 * (trow & 1))) & 0xFFFFu);
-    const uint16_t o = f32_to_bf16(tot + tail);
+    for (int v = 0; v < nw; ++v) tot += red[v][threadIdx.x];
+    const float res = bf16_to_f32((res_word >> (16 * (trow & 1))) & 0xFFFFu);
+    const uint16_t o = f32_to_bf16(tot + res);
     L.out[trow] = o;
     if (L.trace) L.trace[trow] = o;
   }
@@ -630,47 +695,22 @@ constexpr int kNumCU = 256;
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 template <int B>
-hipError_t k1a_launch(const LayerT1& L, int n_router, int n_shared, int lanes, hipStream_t s) {
-  hipLaunchKernelGGL(k1_router<B>, dim3(n_router + n_shared), dim3(kBlock), 0, s, L, n_router,
-                     lanes);
-  return hipPeekAtLastError();
-}
-
-template <int B>
 hipError_t k2_launch(const LayerT1& L, const uint16_t* x, const int32_t* idx, float* act,
-                     int n_gu, int lanes, int n_sd, const RowMap& dm, hipStream_t s) {
-  if (dm.bpl == 1)
-    hipLaunchKernelGGL((k2_gateup<B, 1>), dim3(n_sd + n_gu), dim3(kBlock), 0, s, L, x, idx, act,
-                       lanes, n_sd, dm.lanes);
-  else if (dm.bpl == 2)
-    hipLaunchKernelGGL((k2_gateup<B, 2>), dim3(n_sd + n_gu), dim3(kBlock), 0, s, L, x, idx, act,
-                       lanes, n_sd, dm.lanes);
+                     int n_gu, int lanes, int ns, bool pre, hipStream_t s) {
+  if (pre)
+    hipLaunchKernelGGL((k2_gateup<B, true>), dim3(n_gu), dim3(kBlock), 0, s, L, x, idx, act, lanes,
+                       ns);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k2_gateup<B, false>), dim3(n_gu), dim3(kBlock), 0, s, L, x, idx, act, lanes,
+                       ns);
   return hipPeekAtLastError();
 }
 
 }  // namespace
 
-hipError_t launch_router_t1(const LayerT1& L, bool with_shared, hipStream_t s) {
-  const RowMap gm = gateup_map(L.H);
-  const int n_router = ceil_div(L.E, kWaves);
-  int n_shared = 0;
-  if (with_shared && L.S) {
-    const int tasks = L.F / (32 / gm.lanes);
-    n_shared = ceil_div(tasks, kWaves * 2);  // about two row pairs per wave
-  }
-  switch (gm.bpl) {
-    case 1: return k1a_launch<1>(L, n_router, n_shared, gm.lanes, s);
-    case 2: return k1a_launch<2>(L, n_router, n_shared, gm.lanes, s);
-    case 3: return k1a_launch<3>(L, n_router, n_shared, gm.lanes, s);
-    case 4: return k1a_launch<4>(L, n_router, n_shared, gm.lanes, s);
-    case 5: return k1a_launch<5>(L, n_router, n_shared, gm.lanes, s);
-    case 6: return k1a_launch<6>(L, n_router, n_shared, gm.lanes, s);
-    case 7: return k1a_launch<7>(L, n_router, n_shared, gm.lanes, s);
-    case 8: return k1a_launch<8>(L, n_router, n_shared, gm.lanes, s);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_router_t1(const LayerT1& L, hipStream_t s) {
+  hipLaunchKernelGGL(k1_router, dim3(ceil_div(L.E, kWaves)), dim3(kBlock), 0, s, L);
+  return hipPeekAtLastError();
 }
 
 hipError_t launch_topk_t1(const LayerT1& L, hipStream_t s) {
@@ -679,21 +719,26 @@ hipError_t launch_topk_t1(const LayerT1& L, hipStream_t s) {
 }
 
 hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* idx, float* act,
-                            bool with_shared_down, hipStream_t s) {
-  const RowMap gm = gateup_map(L.H), dm = down_map(L.F);
-  const int tasks = L.k * (L.F / (32 / gm.lanes));
+                            bool with_shared, hipStream_t s) {
+  const RowMap gm = gateup_map(L.H);
+  const int tps = L.F / (32 / gm.lanes);  // tasks per expert
+  const int ns = (with_shared && L.S) ? tps : 0;
+  const int tasks = ns + L.k * tps;
   const int cap = kNumCU * kK2WavesPerCU / kWaves;
-  const int n_gu = ceil_div(tasks, kWaves * 4) < cap ? ceil_div(tasks, kWaves * 4) : cap;
-  const int n_sd = (with_shared_down && L.S) ? ceil_div(L.H / (kWave / dm.lanes), kWaves * kRowsSd) : 0;
+  int n_gu = ceil_div(tasks, kWaves * 4) < cap ? ceil_div(tasks, kWaves * 4) : cap;
+  // with a shared expert every wave starts on a shared task (tps is a
+  // multiple of kWaves for every accepted F)
+  const bool pre = ns > 0;
+  if (pre && n_gu * kWaves > ns) n_gu = ns / kWaves;
   switch (gm.bpl) {
-    case 1: return k2_launch<1>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
-    case 2: return k2_launch<2>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
-    case 3: return k2_launch<3>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
-    case 4: return k2_launch<4>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
-    case 5: return k2_launch<5>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
-    case 6: return k2_launch<6>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
-    case 7: return k2_launch<7>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
-    case 8: return k2_launch<8>(L, x, idx, act, n_gu, gm.lanes, n_sd, dm, s);
+    case 1: return k2_launch<1>(L, x, idx, act, n_gu, gm.lanes, ns, pre, s);
+    case 2: return k2_launch<2>(L, x, idx, act, n_gu, gm.lanes, ns, pre, s);
+    case 3: return k2_launch<3>(L, x, idx, act, n_gu, gm.lanes, ns, pre, s);
+    case 4: return k2_launch<4>(L, x, idx, act, n_gu, gm.lanes, ns, pre, s);
+    case 5: return k2_launch<5>(L, x, idx, act, n_gu, gm.lanes, ns, pre, s);
+    case 6: return k2_launch<6>(L, x, idx, act, n_gu, gm.lanes, ns, pre, s);
+    case 7: return k2_launch<7>(L, x, idx, act, n_gu, gm.lanes, ns, pre, s);
+    case 8: return k2_launch<8>(L, x, idx, act, n_gu, gm.lanes, ns, pre, s);
   }
   return hipErrorInvalidValue;
 }
@@ -706,7 +751,11 @@ hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s) {
   if (gpb * (kWave / dm.lanes) > kK3MaxRows) return hipErrorInvalidValue;
   // one expert's down matrix is addressed through a 32-bit buffer descriptor
   if ((size_t)L.H * (size_t)(L.F / 2) > 0x7FFFFFFFu) return hipErrorInvalidValue;
-  const dim3 g(nblk), b(kK3Block);
+  const int per_wave = dm.bpl == 1 ? 2 : 1;  // routed slots streamed together
+  int nw = ceil_div(L.k, per_wave);
+  if (nw > kK3MaxWaves) nw = kK3MaxWaves;
+  if (nw * kWave < gpb * (kWave / dm.lanes)) nw = ceil_div(gpb * (kWave / dm.lanes), kWave);
+  const dim3 g(nblk), b(nw * kWave);
 #define K3(BP, LN) hipLaunchKernelGGL((k3_down_combine<BP, LN>), g, b, 0, s, L, dm.lanes, gpb)
   if (dm.bpl == 2) K3(2, 64);
   else if (dm.lanes == 64) K3(1, 64);
