@@ -125,9 +125,20 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, const ui
   __syncthreads();
 }
 
-// Plain x staging in two halves, so that other loads can be issued between
-// them: stage_x_load issues the global loads, stage_x_store writes LDS
-// (zero padding included) and ends with a barrier.
+// x staging for the gate/up rows, in two halves so that other loads can be
+// issued between them: stage_x_load issues the global loads, stage_x_store
+// writes LDS (zero padding included) and ends with a barrier.
+//
+// Layout: 16-byte chunk c of x (block b = c / 4 of 32 elements, quarter
+// q = c % 4) is stored at x_chunk_pos(b, q).  A gate/up lane reads the four
+// quarters of its blocks b = col + lanes * i; in the natural order the 32
+// lanes of a half wave would read at a 64-byte stride, four lanes to a bank
+// group.  Here, for one (i, q), consecutive lanes read consecutive chunks.
+// The map permutes each group of 128 chunks, so the padded LDS range
+// (kMaxChunks, a multiple of 128) maps onto itself.
+__device__ __forceinline__ int x_chunk_pos(int b, int q) {
+  return (((b >> 5) << 2) + q) * 32 + (b & 31);
+}
 struct XStage {
   uint4 v[kChunksPerLane];
 };
@@ -146,10 +157,11 @@ __device__ __forceinline__ void stage_x_store(const XStage& st, int H, uint32_t*
 #pragma unroll
   for (int i = 0; i < kChunksPerLane; ++i) {
     const int c = threadIdx.x + i * kBlock;
-    l16[c] = keep_or_zero(c < nch, st.v[i]);
+    l16[x_chunk_pos(c >> 2, c & 3)] = keep_or_zero(c < nch, st.v[i]);
   }
   __syncthreads();
 }
+static_assert(kMaxChunks % 128 == 0, "the chunk map permutes whole groups of 128");
 
 // -------------------------------------------------------------------------
 // Router rows: one wave per row; the row's 16-byte chunks are strided over
@@ -207,7 +219,9 @@ struct GateUpJob {
   float* act;            // [k + 1][F]: routed slots, then the shared expert
 };
 
-template <int BPL>
+// LANES > 0 fixes the lanes per row at compile time: the block offsets of a
+// row then fold into the load instructions' immediate offsets.
+template <int BPL, int LANES = 0>
 struct GateUp {
   int half, rig, col, lanes, rph, tps;
   // this lane's matrices (gate for lanes 0..31, up for 32..63), routed and
@@ -216,7 +230,7 @@ struct GateUp {
 
   __device__ void init(const GateUpJob& J, int lanes_) {
     const int lane = threadIdx.x & 63;
-    lanes = lanes_;
+    lanes = LANES ? LANES : lanes_;
     half = lane >> 5;
     rig = (lane & 31) / lanes;
     col = (lane & 31) % lanes;
@@ -246,11 +260,23 @@ struct GateUp {
     const size_t row = (size_t)(sh ? 0 : e) * J.F + j;
     const uint8_t* cb = (sh ? shc : rc) + row * (size_t)(J.H / 2);
     const uint8_t* sb = (sh ? shs : rs) + row * (size_t)(J.H / 32);
+    if (LANES) {
+      // lane base once, constant strides: immediate offsets on the loads
+      const u32x4* cp = reinterpret_cast<const u32x4*>(cb) + col;
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(sb) + (col >> 2);
 #pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      const int b = col + lanes * i;
-      c[i] = ld_stream16(cb + (size_t)b * 16);
-      sc[i] = ld_stream_word_of(sb, b);
+      for (int i = 0; i < BPL; ++i) {
+        const u32x4 t = __builtin_nontemporal_load(cp + LANES * i);
+        c[i] = make_uint4(t.x, t.y, t.z, t.w);
+        sc[i] = __builtin_nontemporal_load(sp + (LANES / 4) * i);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        const int b = col + lanes * i;
+        c[i] = ld_stream16(cb + (size_t)b * 16);
+        sc[i] = ld_stream_word_of(sb, b);
+      }
     }
   }
   __device__ __forceinline__ void finish(const GateUpJob& J, const uint32_t* x_lds, int t,
@@ -258,11 +284,12 @@ struct GateUp {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
-      const uint4* xl = reinterpret_cast<const uint4*>(x_lds) + (col + lanes * i) * 4;
+      const uint4* xl = reinterpret_cast<const uint4*>(x_lds);
+      const int b = col + lanes * i;
       uint32_t xv[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 v = xl[q];
+        const uint4 v = xl[x_chunk_pos(b, q)];
         xv[4 * q + 0] = v.x;
         xv[4 * q + 1] = v.y;
         xv[4 * q + 2] = v.z;
@@ -274,7 +301,8 @@ struct GateUp {
       // keep the x reads of later blocks from being hoisted (register use)
       __builtin_amdgcn_sched_barrier(0);
     }
-    acc = group_sum_last(acc, lanes);
+    if (LANES) acc = group_sum_last_c<LANES ? LANES : 32>(acc);
+    else acc = group_sum_last(acc, lanes);
     const float up = __shfl_xor(acc, 32, kWave);
     if (half == 0 && col == lanes - 1) {
       bool sh;
@@ -291,8 +319,8 @@ struct GateUp {
 // count and the last one or two tasks are peeled, so no load sits under a
 // branch that rejoins: at such a join the compiler's wait counts assume the
 // path without the load and would wait for the newer loads as well.
-template <int BPL>
-__device__ void gateup_tasks(const GateUp<BPL>& g, const GateUpJob& J, const uint32_t* x_lds,
+template <int BPL, int LANES>
+__device__ void gateup_tasks(const GateUp<BPL, LANES>& g, const GateUpJob& J, const uint32_t* x_lds,
                              int ntask, int first, int stride, uint4 (&ca)[BPL],
                              uint32_t (&sa)[BPL]) {
   if (first >= ntask) return;
@@ -336,6 +364,14 @@ struct DownLanes {
   __device__ __forceinline__ float reduce(float v) const {
     if (LANES) return group_sum_last_c<LANES ? LANES : 64>(v);
     return group_sum_last(v, lanes);
+  }
+  // Pins the activations: the wait for their loads happens here, not
+  // inside a later loop (an empty asm that claims to modify the registers).
+  __device__ __forceinline__ void settle_act() {
+#pragma unroll
+    for (int i = 0; i < BPL; ++i)
+#pragma unroll
+      for (int q = 0; q < 32; ++q) asm volatile("" : "+v"(ar[i][q]));
   }
   __device__ void load_act(const float* a) {
     const float4* a16 = reinterpret_cast<const float4*>(a);
@@ -423,15 +459,19 @@ __global__ __launch_bounds__(kBlock) void k1_topk(LayerT1 L) {
   topk_softmax_block(lg, L.E, L.k, tk, L.idx, L.wts, L.idx_out, L.w_out);
 }
 
+// Two waves per SIMD for the gate/up kernel: three (at most 168 registers)
+// measured no faster, and the selection then covers fewer shared tasks.
+constexpr int kK2WavesPerSimd = 2;
+
 // K2: gate/up of the shared expert and of the k selected experts.  With
 // idx == null the experts are selected here: every workgroup runs the same
 // top-k on the router logits (deterministic, identical in every workgroup)
 // and workgroup 0 publishes the indices and weights for K3 and the caller.
-// PRE (a shared expert, and no more waves than shared tasks): every wave's
-// first task is a shared one, requested before the selection, so the
-// selection latency is spent under shared-expert bytes.
-template <int BPLH, bool PRE>
-__global__ __launch_bounds__(kBlock) void k2_gateup(LayerT1 L, const uint16_t* __restrict__ x,
+// With a shared expert (PRE) a wave whose first task is a shared one
+// requests it before the selection, so the selection latency is spent under
+// shared-expert bytes.
+template <int BPLH, int LANES, bool PRE>
+__global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, const uint16_t* __restrict__ x,
                                                     const int32_t* __restrict__ idx,
                                                     float* __restrict__ act, int gu_lanes, int ns) {
   __shared__ __align__(16) uint32_t x_lds[kMaxH / 2];
@@ -442,7 +482,7 @@ __global__ __launch_bounds__(kBlock) void k2_gateup(LayerT1 L, const uint16_t* _
   const GateUpJob J{L.g_codes,  L.g_scales,  L.u_codes,  L.u_scales, L.sg_codes, L.sg_scales,
                     L.su_codes, L.su_scales, e_lds,      L.H,        L.F,        L.k,
                     ns,         act};
-  GateUp<BPLH> g;
+  GateUp<BPLH, LANES> g;
   g.init(J, gu_lanes);
   const int first = blockIdx.x * kWaves + wid, ntask = ns + L.k * g.tps;
   // Request order matters: loads complete in order for the wait counter, so
@@ -463,7 +503,8 @@ __global__ __launch_bounds__(kBlock) void k2_gateup(LayerT1 L, const uint16_t* _
   stage_x_load(x, L.H, xs);
   uint4 ca[BPLH];
   uint32_t sa[BPLH];
-  if constexpr (PRE) g.load(J, first, ca, sa);  // first < ns: a shared task
+  const bool early = PRE && first < ns;  // wave-uniform
+  if (early) g.load(J, first, ca, sa);
   if (idx) {
     if (threadIdx.x < L.k)
       e_lds[threadIdx.x] = e_in < 0 ? 0 : (e_in >= L.E ? L.E - 1 : e_in);  // never address outside
@@ -472,7 +513,7 @@ __global__ __launch_bounds__(kBlock) void k2_gateup(LayerT1 L, const uint16_t* _
     topk_softmax_block(lg, L.E, L.k, tk, e_lds, w_lds, nullptr, nullptr);
     __syncthreads();
   }
-  if constexpr (!PRE) g.load(J, first < ntask ? first : ntask - 1, ca, sa);
+  if (!early) g.load(J, first < ntask ? first : ntask - 1, ca, sa);
   stage_x_store(xs, L.H, x_lds);
   if (!idx && blockIdx.x == 0 && threadIdx.x < L.k) {
     const int e = e_lds[threadIdx.x];
@@ -545,30 +586,33 @@ __device__ __forceinline__ DownSlot shared_slot(const LayerT1& L) {
 
 // One wave's pass over the slab for one or two routed slots (TWO),
 // accumulating into its LDS partial row `red`; `between` runs once the
-// first burst and the activations have been requested.  Every request is
-// unconditional (the burst index is clamped): a load under a branch that
-// rejoins makes the compiler wait for the newer loads as well.  The one
-// redundant burst per pass re-reads rows this wave has just requested, so
-// it is served by L2.
-template <int BPLF, int LANES, bool TWO, typename Between>
+// first bursts and the activations have been requested.  DEPTH bursts are
+// in flight while one is reduced.  Every request is unconditional: a load
+// under a branch that rejoins makes the compiler wait for the newer loads
+// as well.  Bursts past the slab end are issued against an empty
+// descriptor: they return zeros without a memory access (a scalar select,
+// so the lane offsets stay loop-invariant registers).
+template <int BPLF, int LANES, bool TWO, int DEPTH, typename Between>
 __device__ __forceinline__ void down_pass(const LayerT1& L, const DownSlot& A, const DownSlot& B,
                                           DownLanes<BPLF, LANES>& dA, DownLanes<BPLF, LANES>& dB,
                                           int gbase, int ng, float* red, Between between) {
   constexpr int NB = kK3Burst;
-  auto load_burst = [&](int g0, DownBurst<BPLF, LANES>& P) {
+  const int nb = (ng + NB - 1) / NB;
+  const __amdgpu_buffer_rsrc_t none = buf_rsrc(nullptr, 0u);
+  auto load_burst = [&](int i, DownBurst<BPLF, LANES>& P) {
+    const bool skip = i >= nb;
+    const auto rca = skip ? none : A.rc, rsa = skip ? none : A.rs;
+    const auto rcb = skip ? none : B.rc, rsb = skip ? none : B.rs;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int row0 = (gbase + (g0 + j < ng ? g0 + j : ng - 1)) * dA.rpw;
-      dA.load_row_buf(A.rc, A.rs, L.F, row0, P.ca[j], P.xa[j]);
-      if (TWO) dB.load_row_buf(B.rc, B.rs, L.F, row0, P.cb[j], P.xb[j]);
+      const int g = i * NB + j;
+      const int row0 = (gbase + (g < ng ? g : ng - 1)) * dA.rpw;
+      dA.load_row_buf(rca, rsa, L.F, row0, P.ca[j], P.xa[j]);
+      if (TWO) dB.load_row_buf(rcb, rsb, L.F, row0, P.cb[j], P.xb[j]);
     }
   };
-  DownBurst<BPLF, LANES> P, Q;
-  load_burst(0, P);
-  dA.load_act(A.act);
-  if (TWO) dB.load_act(B.act);
-  between();
-  auto use_burst = [&](int g0, const DownBurst<BPLF, LANES>& P) {
+  auto use_burst = [&](int i, const DownBurst<BPLF, LANES>& P) {
+    const int g0 = i * NB;
     float v[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -584,15 +628,47 @@ __device__ __forceinline__ void down_pass(const LayerT1& L, const DownSlot& A, c
     for (int j = 0; j < NB; ++j)
       if (g0 + j < ng && dA.col == dA.lanes - 1) red[(g0 + j) * dA.rpw + dA.rig] += v[j];
   };
-  const int nb = (ng + NB - 1) / NB;
-  for (int i = 0; i < nb; i += 2) {
-    load_burst((i + 1 < nb ? i + 1 : nb - 1) * NB, Q);
-    __builtin_amdgcn_sched_barrier(0);
-    use_burst(i * NB, P);
-    if (i + 1 >= nb) break;
-    load_burst((i + 2 < nb ? i + 2 : nb - 1) * NB, P);
-    __builtin_amdgcn_sched_barrier(0);
-    use_burst((i + 1) * NB, Q);
+  // Activations first: the loop is then entered, as it is re-entered, with
+  // exactly the weight bursts outstanding, and the compiler's wait counts
+  // in the loop need not cover a younger activation load.
+  dA.load_act(A.act);
+  if (TWO) dB.load_act(B.act);
+  DownBurst<BPLF, LANES> P, Q;
+  load_burst(0, P);
+  if constexpr (DEPTH == 3) {
+    DownBurst<BPLF, LANES> R;
+    load_burst(1, Q);
+    // Wait for the activations now, with two bursts in flight: entering the
+    // loop with them still outstanding would put 64 loads in flight at its
+    // first request, past what the wait counter tracks, and every later
+    // wait in the loop would be too deep.
+    dA.settle_act();
+    if (TWO) dB.settle_act();
+    between();
+    for (int i = 0; i < nb; i += 3) {
+      load_burst(i + 2, R);
+      __builtin_amdgcn_sched_barrier(0);
+      use_burst(i, P);
+      if (i + 1 >= nb) break;
+      load_burst(i + 3, P);
+      __builtin_amdgcn_sched_barrier(0);
+      use_burst(i + 1, Q);
+      if (i + 2 >= nb) break;
+      load_burst(i + 4, Q);
+      __builtin_amdgcn_sched_barrier(0);
+      use_burst(i + 2, R);
+    }
+  } else {
+    between();
+    for (int i = 0; i < nb; i += 2) {
+      load_burst(i + 1, Q);
+      __builtin_amdgcn_sched_barrier(0);
+      use_burst(i, P);
+      if (i + 1 >= nb) break;
+      load_burst(i + 2, P);
+      __builtin_amdgcn_sched_barrier(0);
+      use_burst(i + 1, Q);
+    }
   }
 }
 
@@ -649,11 +725,13 @@ __global__ __launch_bounds__(kK3MaxWaves * kWave) void k3_down_combine(LayerT1 L
   auto routed = [&](int s0, auto between) {
     const int sb = s0 + nw;
     const DownSlot A = routed_slot(L, s0, e_v, w_v);
+    // three bursts in flight where the registers allow it (one block per lane)
+    constexpr int DEPTH = BPLF == 1 ? 3 : 2;
     if (PAIRS && sb < L.k) {
       const DownSlot B = routed_slot(L, sb, e_v, w_v);
-      down_pass<BPLF, LANES, PAIRS>(L, A, B, dA, dB, gbase, ng, red[wid], between);
+      down_pass<BPLF, LANES, PAIRS, DEPTH>(L, A, B, dA, dB, gbase, ng, red[wid], between);
     } else {
-      down_pass<BPLF, LANES, false>(L, A, A, dA, dB, gbase, ng, red[wid], between);
+      down_pass<BPLF, LANES, false, DEPTH>(L, A, A, dA, dB, gbase, ng, red[wid], between);
     }
   };
   // The first pass is not part of the loop: inside it the shared rows would
@@ -688,8 +766,172 @@ __global__ __launch_bounds__(kK3MaxWaves * kWave) void k3_down_combine(LayerT1 L
   }
 }
 
+// K3, activations in LDS (one block per lane, F a multiple of 32 x lanes,
+// and every slot's activations within kK3LdsActBytes).  The workgroup first
+// copies the activations of all slots into LDS; then the work is a list of
+// bursts, (slot, kK3Burst row groups of the slab), the shared expert's
+// first, dealt round robin to kK3LdsWaves waves.  A wave keeps three bursts
+// in flight and reads the slot's activations from LDS once per burst, so it
+// needs few registers: four waves per SIMD.  Requests past the end of a
+// wave's list go to an empty descriptor (zeros, no memory traffic).  Row
+// results go to the wave's LDS partial row; partials are summed in wave
+// order with the residual, as in the register variant.
+constexpr int kK3LdsWaves = 16;
+constexpr int kK3LdsActBytes = 144 * 1024;
+static_assert(kK3LdsActBytes % (16 * kK3LdsWaves * kWave) == 0, "whole staging rounds");
+
+template <int LANES>
+struct LdsBurst {
+  uint4 c[kK3Burst];
+  uint32_t x[kK3Burst];
+  int as, c0;  // activation slot and first row group (wave-uniform)
+  float w;     // combine weight
+};
+
+template <int LANES>
+__global__ __launch_bounds__(kK3LdsWaves * kWave) void k3_down_lds(LayerT1 L, int gpb) {
+  extern __shared__ __align__(16) float k3_smem[];
+  float* act_lds = k3_smem;                                        // [slots][8][F/32][4]
+  float* red = k3_smem + (size_t)(L.k + (L.S ? 1 : 0)) * L.F;   // [waves][kK3MaxRows]
+  constexpr int NB = kK3Burst;
+  // one block per lane: F = 32 LANES, and a row group (64 / LANES rows) is
+  // always 1 KB of codes and 64 bytes of scales
+  constexpr uint32_t kGroupCodes = 1024, kGroupScales = 64;
+  const int wid = wave_id(), lane = threadIdx.x & 63;
+  const int nslots = L.k + (L.S ? 1 : 0);
+  // routed experts and weights, lane i holding slot i (k <= 32 < 64)
+  const int e_v = L.idx[lane < L.k ? lane : 0];
+  const float w_v = L.wts[lane < L.k ? lane : 0];
+  DownLanes<1, LANES> d;
+  d.init_map(LANES);
+  const int ngroups = L.H / d.rpw;
+  const int gbase = blockIdx.x * gpb;
+  const int ng = ngroups - gbase < gpb ? ngroups - gbase : gpb;  // groups of this slab
+  const int R = ng * d.rpw;
+  float* red_w = red + wid * kK3MaxRows;
+  for (int t = lane; t < R; t += kWave) red_w[t] = 0.f;
+  const int trow = gbase * d.rpw + (threadIdx.x < R ? threadIdx.x : 0);
+  const uint32_t res_word = buf_ld4(buf_rsrc(L.residual, L.residual ? (uint32_t)L.H * 2u : 0u),
+                                    ((uint32_t)trow * 2u) & ~3u, 0u);
+  // activations -> LDS: float4 j of a slot (elements 4j..4j+3, block j/8,
+  // chunk j%8) goes to position (j%8) * nbk + j/8, so that a chunk read of
+  // consecutive blocks by consecutive lanes touches consecutive addresses
+  const int nbk = L.F / 32, f4_per_slot = L.F / 4, f4_total = nslots * f4_per_slot;
+  // one staging round covers kK3LdsActBytes (the launcher's bound)
+  constexpr int kStage = kK3LdsActBytes / 16 / (kK3LdsWaves * kWave);
+  f32x4 st[kStage];  // native vectors: an array of HIP's float4 struct lands in scratch
+#pragma unroll
+  for (int u = 0; u < kStage; ++u) {
+    const int j = u * (int)blockDim.x + (int)threadIdx.x;
+    st[u] = reinterpret_cast<const f32x4*>(L.act)[j < f4_total ? j : f4_total - 1];
+  }
+
+  // this wave's bursts: b = wid, wid + nw, ...; burst b covers list slot
+  // p = b / nch (0: the shared expert when present) and chunk b % nch
+  const int nch = (ng + NB - 1) / NB, nbt = nslots * nch;
+  constexpr int nw = kK3LdsWaves;
+  // b / nch as a multiply and shift (scalar divisions are long sequences):
+  // exact for b < 2^16 / 64 with nch <= 64 (here b < 33 * 16, nch <= 16)
+  const int inv_nch = (65536 + nch - 1) / nch;
+  const size_t mat_c = (size_t)L.H * (L.F / 2), mat_s = (size_t)L.H * (L.F / 32);
+  // lane offsets within a row group (loop-invariant vector registers)
+  const uint32_t voc = (uint32_t)d.rig * (uint32_t)(L.F / 2) + (uint32_t)d.col * 16u;
+  const uint32_t vos = ((uint32_t)d.rig * (uint32_t)(L.F / 32) + (uint32_t)d.col) & ~3u;
+  // Burst i of this wave: slot, weight and row groups are computed once,
+  // here, and travel with the buffer.  The matrix base and the size are
+  // selected as scalars and one descriptor is built from them (selecting
+  // whole descriptors compiles to branches).  Row groups past the slab end
+  // read the next rows of the matrix, or zeros past its end; their results
+  // are dropped.
+  auto load_burst = [&](int i, LdsBurst<LANES>& P) {
+    const int b = wid + i * nw;
+    const int bb = b < nbt ? b : nbt - 1;
+    const int p = (bb * inv_nch) >> 16;
+    const bool sh = L.S && p == 0;
+    const int s = sh ? 0 : p - (L.S ? 1 : 0);  // routed slot
+    const int e0 = __builtin_amdgcn_readlane(e_v, s);
+    const int e = sh ? 0 : (e0 < 0 ? 0 : (e0 >= L.E ? L.E - 1 : e0));  // never address outside
+    P.as = sh ? L.k : s;
+    P.w = sh ? 1.f : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_v), s));
+    P.c0 = (bb - p * nch) * NB;
+    const bool live = b < nbt;
+    const auto rc = buf_rsrc((sh ? L.sd_codes : L.d_codes) + (size_t)e * mat_c,
+                             live ? (uint32_t)mat_c : 0u);
+    const auto rs = buf_rsrc((sh ? L.sd_scales : L.d_scales) + (size_t)e * mat_s,
+                             live ? (uint32_t)mat_s : 0u);
+    const uint32_t g0 = (uint32_t)(gbase + P.c0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      P.c[j] = buf_ld16(rc, voc + j * kGroupCodes, g0 * kGroupCodes);
+      P.x[j] = buf_ld4(rs, vos + j * kGroupScales, g0 * kGroupScales);
+    }
+  };
+  auto use_burst = [&](int i, const LdsBurst<LANES>& P) {
+    const bool live = wid + i * nw < nbt;
+    // this lane's 32 activations of the slot, chunk by chunk
+    const f32x4* a4 = reinterpret_cast<const f32x4*>(act_lds) + (size_t)P.as * f4_per_slot + d.col;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f32x4 v = a4[q * nbk];
+      d.ar[0][4 * q + 0] = v.x;
+      d.ar[0][4 * q + 1] = v.y;
+      d.ar[0][4 * q + 2] = v.z;
+      d.ar[0][4 * q + 3] = v.w;
+    }
+    float v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const uint4 c1[1] = {P.c[j]};
+      const uint32_t x1[1] = {P.x[j]};
+      v[j] = P.w * d.dot(c1, x1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) v[j] = d.reduce(v[j]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (live && P.c0 + j < ng && d.col == d.lanes - 1) red_w[(P.c0 + j) * d.rpw + d.rig] += v[j];
+  };
+
+  LdsBurst<LANES> P, Q, Rb;
+  load_burst(0, P);
+  load_burst(1, Q);
+#pragma unroll
+  for (int u = 0; u < kStage; ++u) {
+    const int j = u * (int)blockDim.x + (int)threadIdx.x;
+    if (j < f4_total) {
+      const int sl = j / f4_per_slot, jj = j - sl * f4_per_slot;
+      reinterpret_cast<f32x4*>(act_lds)[sl * f4_per_slot + (jj & 7) * nbk + (jj >> 3)] = st[u];
+    }
+  }
+  __syncthreads();  // activations in LDS
+  const int nb = (nbt - wid + nw - 1) / nw;  // bursts of this wave
+  for (int i = 0; i < nb; i += 3) {
+    load_burst(i + 2, Rb);
+    __builtin_amdgcn_sched_barrier(0);
+    use_burst(i, P);
+    if (i + 1 >= nb) break;
+    load_burst(i + 3, P);
+    __builtin_amdgcn_sched_barrier(0);
+    use_burst(i + 1, Q);
+    if (i + 2 >= nb) break;
+    load_burst(i + 4, Q);
+    __builtin_amdgcn_sched_barrier(0);
+    use_burst(i + 2, Rb);
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < R) {  // R <= kK3MaxRows <= the workgroup size
+    float tot = 0.f;
+    for (int v = 0; v < nw; ++v) tot += red[v * kK3MaxRows + threadIdx.x];
+    const float res = bf16_to_f32((res_word >> (16 * (trow & 1))) & 0xFFFFu);
+    const uint16_t o = f32_to_bf16(tot + res);
+    L.out[trow] = o;
+    if (L.trace) L.trace[trow] = o;
+  }
+}
+
 // ---------------------------------------------------------------- dispatch
-constexpr int kK2WavesPerCU = 8;
+constexpr int kK2WavesPerCU = 4 * kK2WavesPerSimd;
 constexpr int kNumCU = 256;
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
@@ -697,12 +939,27 @@ int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 template <int B>
 hipError_t k2_launch(const LayerT1& L, const uint16_t* x, const int32_t* idx, float* act,
                      int n_gu, int lanes, int ns, bool pre, hipStream_t s) {
-  if (pre)
-    hipLaunchKernelGGL((k2_gateup<B, true>), dim3(n_gu), dim3(kBlock), 0, s, L, x, idx, act, lanes,
-                       ns);
-  else
-    hipLaunchKernelGGL((k2_gateup<B, false>), dim3(n_gu), dim3(kBlock), 0, s, L, x, idx, act, lanes,
-                       ns);
+#define K2(LN, P) \
+  hipLaunchKernelGGL((k2_gateup<B, LN, P>), dim3(n_gu), dim3(kBlock), 0, s, L, x, idx, act, lanes, ns)
+  if (lanes == 32) {  // the common case (H a multiple of 1024): offsets fold
+    if (pre) K2(32, true);
+    else K2(32, false);
+  } else {
+    if (pre) K2(0, true);
+    else K2(0, false);
+  }
+#undef K2
+  return hipPeekAtLastError();
+}
+
+// More than 64 KB of dynamic LDS needs the function's limit raised first
+// (set on every launch: cheap, and correct on whichever device is current).
+template <int LN>
+hipError_t k3_lds_launch(const LayerT1& L, int gpb, int nblk, size_t lds, hipStream_t s) {
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k3_down_lds<LN>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k3_down_lds<LN>), dim3(nblk), dim3(kK3LdsWaves * kWave), lds, s, L, gpb);
   return hipPeekAtLastError();
 }
 
@@ -727,7 +984,7 @@ hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* 
   const int cap = kNumCU * kK2WavesPerCU / kWaves;
   int n_gu = ceil_div(tasks, kWaves * 4) < cap ? ceil_div(tasks, kWaves * 4) : cap;
   // with a shared expert every wave starts on a shared task (tps is a
-  // multiple of kWaves for every accepted F)
+  // multiple of kWaves for every accepted F), requested before the selection
   const bool pre = ns > 0;
   if (pre && n_gu * kWaves > ns) n_gu = ns / kWaves;
   switch (gm.bpl) {
@@ -751,6 +1008,18 @@ hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s) {
   if (gpb * (kWave / dm.lanes) > kK3MaxRows) return hipErrorInvalidValue;
   // one expert's down matrix is addressed through a 32-bit buffer descriptor
   if ((size_t)L.H * (size_t)(L.F / 2) > 0x7FFFFFFFu) return hipErrorInvalidValue;
+  const size_t act_bytes = (size_t)(L.k + (L.S ? 1 : 0)) * L.F * sizeof(float);
+  if (dm.bpl == 1 && act_bytes <= (size_t)kK3LdsActBytes) {
+    const size_t lds = act_bytes + (size_t)kK3LdsWaves * kK3MaxRows * sizeof(float);
+    switch (dm.lanes) {
+      case 64: return k3_lds_launch<64>(L, gpb, nblk, lds, s);
+      case 32: return k3_lds_launch<32>(L, gpb, nblk, lds, s);
+      case 16: return k3_lds_launch<16>(L, gpb, nblk, lds, s);
+      case 8: return k3_lds_launch<8>(L, gpb, nblk, lds, s);
+      case 4: return k3_lds_launch<4>(L, gpb, nblk, lds, s);
+    }
+    return hipErrorInvalidValue;
+  }
   const int per_wave = dm.bpl == 1 ? 2 : 1;  // routed slots streamed together
   int nw = ceil_div(L.k, per_wave);
   if (nw > kK3MaxWaves) nw = kK3MaxWaves;
