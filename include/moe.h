@@ -48,8 +48,7 @@
  *    0 <= T <= 64 tokens (T = 0 is a no-op returning MOE_OK)
  *    H % 256 == 0, 256 <= H <= 8192, and (H/256)/gcd(H/256, 4) <= 8
  *      (every multiple of 256 up to 2048, and e.g. 3072, 4096, 7168, 8192)
- *    F % 128 == 0 and F/32/gcd(F/32, 64) <= 2
- *      (F in {128, 256, 512, 1024, 2048, 4096})
+ *    F % 128 == 0, 128 <= F <= 8192
  *    1 <= k <= min(E, 32), 1 <= E <= 1024
  *    n_shared in {0, 1}; with a shared expert, shared_ffn == ffn
  */

@@ -27,7 +27,7 @@ struct Carver {
 
 // Single-token layout.
 struct WsT1 {
-  size_t reserved, logits, idx, wts, act, xn, total;
+  size_t reserved, logits, idx, wts, act_hl, part, xn, total;
 };
 
 WsT1 ws_t1(const moe_shape& s) {
@@ -38,7 +38,8 @@ WsT1 ws_t1(const moe_shape& s) {
   L.logits = c.take(sizeof(float) * s.n_experts);
   L.idx = c.take(sizeof(int32_t) * s.top_k);
   L.wts = c.take(sizeof(float) * s.top_k);
-  L.act = c.take(sizeof(float) * nslot * s.ffn);
+  L.act_hl = c.take(sizeof(uint16_t) * 2 * nslot * s.ffn);
+  L.part = c.take(sizeof(float) * nslot * s.hidden);
   L.xn = c.take(sizeof(uint16_t) * s.hidden);
   L.total = c.o;
   return L;
@@ -100,8 +101,7 @@ int check_shape(const moe_shape* s) {
   if (s->n_experts > moe::kMaxExperts || s->top_k > moe::kMaxTopK) return MOE_ERR_UNSUPPORTED;
   if (s->hidden % 256 || s->hidden > 8192) return MOE_ERR_UNSUPPORTED;
   if (moe::gateup_map(s->hidden).bpl > moe::kMaxBplGateUp) return MOE_ERR_UNSUPPORTED;
-  if (s->ffn % 128) return MOE_ERR_UNSUPPORTED;
-  if (moe::down_map(s->ffn).bpl > moe::kMaxBplDown) return MOE_ERR_UNSUPPORTED;
+  if (s->ffn % 128 || s->ffn > moe::kMaxFfn) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -174,7 +174,9 @@ LayerT1 make_layer(const moe_shape* s, const moe_layer_weights* w, void* ws) {
   L.logits = (float*)(b + W.logits);
   L.idx = (int32_t*)(b + W.idx);
   L.wts = (float*)(b + W.wts);
-  L.act = (float*)(b + W.act);
+  L.act_hl = (uint16_t*)(b + W.act_hl);
+  L.part = (float*)(b + W.part);
+  L.counters = (uint32_t*)(b + W.reserved);
   L.xn = (uint16_t*)(b + W.xn);
   return L;
 }
@@ -218,7 +220,7 @@ int run_layer_t1(LayerT1& L, hipStream_t st) {
   hipError_t e = moe::launch_router_t1(L, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const uint16_t* xin = L.gamma ? L.xn : L.x;
-  e = moe::launch_gateup_t1(L, xin, nullptr, L.act, true, st);
+  e = moe::launch_gateup_t1(L, xin, nullptr, nullptr, true, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_down_combine_t1(L, st));
 }

@@ -42,8 +42,6 @@
 namespace moe {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kBlk = 256;
 constexpr int kWv = kBlk / kWave;
@@ -53,27 +51,6 @@ constexpr int kMaxRouterSplits = 16;
 
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Eight MXFP4 elements (one code dword, element order) times the block scale,
-// as exact bf16 values.
-__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
-  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
-  const bf16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-  return r;
-}
-
-__device__ __forceinline__ uint32_t dword_of(const uint4& v, int s) {
-  return s == 0 ? v.x : (s == 1 ? v.y : (s == 2 ? v.z : v.w));
-}
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Inclusive scan over a workgroup of kGroupBlock threads (16 waves).
@@ -127,7 +104,7 @@ __global__ __launch_bounds__(kBlk) void kb_router(LayerTB L, int n_et) {
     for (int nt = 0; nt < 4; ++nt)
       if (nt < NT) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc[nt] = mfma(as_bf16x8(a[s]), as_bf16x8(b[nt][s]), acc[nt]);
+        for (int s = 0; s < 4; ++s) acc[nt] = mfma16(as_bf16x8(a[s]), as_bf16x8(b[nt][s]), acc[nt]);
       }
   }
 #pragma unroll
@@ -302,8 +279,8 @@ __device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, const uint4 (*bt)[KC
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 bv = as_bf16x8(bt[r][kk * 16 + 4 * q + s]);
-      cg = mfma(fp4x8_to_bf16(dword_of(R.ag[kk], s), fg), bv, cg);
-      cu = mfma(fp4x8_to_bf16(dword_of(R.au[kk], s), fu), bv, cu);
+      cg = mfma16(fp4x8_to_bf16(dword_of(R.ag[kk], s), fg), bv, cg);
+      cu = mfma16(fp4x8_to_bf16(dword_of(R.au[kk], s), fu), bv, cu);
     }
   }
 }
@@ -410,8 +387,8 @@ __device__ __forceinline__ void dn_mma(const DnRegs<KC>& R, const uint4 (*bh)[KC
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 av = fp4x8_to_bf16(dword_of(R.a[kk], s), f);
-      acc = mfma(av, as_bf16x8(bh[r][kk * 16 + 4 * q + s]), acc);
-      acc = mfma(av, as_bf16x8(bl[r][kk * 16 + 4 * q + s]), acc);
+      acc = mfma16(av, as_bf16x8(bh[r][kk * 16 + 4 * q + s]), acc);
+      acc = mfma16(av, as_bf16x8(bl[r][kk * 16 + 4 * q + s]), acc);
     }
   }
 }

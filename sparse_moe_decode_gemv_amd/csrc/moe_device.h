@@ -16,6 +16,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
 constexpr int kWave = 64;
 
@@ -54,6 +55,13 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 }
 __device__ __forceinline__ uint32_t buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kBufNT);
+}
+// A wave-uniform read of data no kernel of the launch writes, through the
+// scalar data cache (a scalar load: it waits on lgkmcnt, not on the vector
+// memory counter that tracks the weight stream).
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
 }
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int byte) {
   return __builtin_amdgcn_ubfe(w, 8 * byte, 8);
@@ -211,6 +219,32 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
 __device__ __forceinline__ float f32_from_order_key(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
   return __uint_as_float(u);
+}
+
+// ---- v_mfma_f32_16x16x32_bf16 fragments ------------------------------------
+// Lane l = 16 q + r holds A[r][8q .. 8q+7] and B[8q .. 8q+7][r]; the result
+// lane holds C[4q .. 4q+3][r].  The reduction index may be permuted freely as
+// long as A and B use the same permutation.
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Eight MXFP4 elements (one code dword, element order) times the block
+// scale, as exact bf16 values.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  const bf16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int s) {
+  return s == 0 ? v.x : (s == 1 ? v.y : (s == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 }  // namespace moe

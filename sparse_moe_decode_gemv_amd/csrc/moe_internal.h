@@ -21,15 +21,8 @@ inline RowMap gateup_map(int H) {
   while (nb % g) g >>= 1;
   return {g, nb / g};
 }
-// down rows (reduction over F): the whole wave.
-inline RowMap down_map(int F) {
-  int nb = F / 32, g = 64;
-  while (nb % g) g >>= 1;
-  return {g, nb / g};
-}
-
 constexpr int kMaxBplGateUp = 8;
-constexpr int kMaxBplDown = 2;
+constexpr int kMaxFfn = 8192;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxTokens = 64;
@@ -53,7 +46,10 @@ struct LayerT1 {
   float* logits;       // [E]
   int32_t* idx;        // [k]
   float* wts;          // [k]
-  float* act;          // [k + S][F]: routed slots, then the shared expert
+  uint16_t* act_hl;    // bf16 [2][k + S][F]: gated activations split as
+                       // leading part + remainder (routed slots, then shared)
+  float* part;         // [k + S][H]: weighted down-projection rows per slot
+  uint32_t* counters;  // per row chunk, zero between calls (workspace head)
   uint16_t* xn;        // [H] normalised input (stack)
   // optional user outputs
   float* logits_out;
@@ -62,7 +58,8 @@ struct LayerT1 {
 };
 
 // K1a router, K2 top-k when idx is null and gate/up (shared expert first
-// when with_shared), K3 down of every slot (the shared expert last) +
+// when with_shared; fp32 activations into act, or split bf16 into L.act_hl
+// when act is null), K3 down of every slot (the shared expert last) +
 // combine; launch_topk_t1 is the stand-alone top-k of the router entry point.
 hipError_t launch_router_t1(const LayerT1& L, hipStream_t s);
 hipError_t launch_topk_t1(const LayerT1& L, hipStream_t s);

@@ -3,8 +3,9 @@
 //  K1a router GEMV over all E rows (one wave per row, every load of the row
 //      in flight at once).
 //  K2  top-k + softmax (radix select) in every workgroup, then gate/up GEMVs
-//      with fused MXFP4 dequant and SiLU gating -> fp32 activations: first
-//      the shared expert's rows, then those of the k selected experts.  The
+//      with fused MXFP4 dequant and SiLU gating -> gated activations (fp32
+//      for the gate/up entry point; in the layer, two bf16 parts for K3):
+//      first the shared expert's rows, then those of the k selected experts.  The
 //      shared expert does not depend on routing (the pages run it beside the
 //      selected experts: page "AI手搓1.2万行代码榨干GB300!…", section 02;
 //      smzdm page, section "四步改造"), so every wave requests its shared
@@ -12,21 +13,27 @@
 //      shared-expert bytes.
 //  K3  down GEMVs of the k selected experts and of the shared expert,
 //      router-weighted combine (shared weight 1) and residual add -> bf16.
-//      One workgroup per CU owns a slab of output rows, each wave streams
-//      two slots' rows of the slab, and the slots are summed in LDS in a
-//      fixed order (deterministic, no floating-point atomics).
+//      The gated activations arrive split into two bf16 parts (leading part
+//      + remainder), so the products run on v_mfma_f32_4x4x4_16b_bf16 with
+//      about 16 significant bits of the activation, and the vector ALU only
+//      decodes MXFP4.  When every slot's activations fit in LDS, one
+//      workgroup per CU owns a slab of output rows for every slot and sums
+//      the slots in LDS in a fixed order (deterministic, no floating-point
+//      atomics); otherwise a workgroup owns one slot's rows of one chunk and
+//      the chunk's last workgroup combines (see k3_down).
 //
 // Decode is bound by streaming weights from HBM (page "英伟达用1.2万行CuTe DSL
 // Megakernel…", section "解码优化为何比训练优化更难"; tmtpost page, section
 // "为什么是解码"), so every kernel reads each weight byte once with 16-byte
-// nontemporal loads, keeps the activation vector in registers, and decodes
-// MXFP4 in registers right before the dot product.
+// nontemporal loads and decodes MXFP4 in registers right before use.
 //
-// Data passes between kernels only through stream order: no workgroup reads
-// what another workgroup of the same launch wrote, so no cross-CU fences or
-// flags are needed (the ordering bug the pages report came from activation
-// loads moved above a wait: page "英伟达用1.2万行CuTe DSL Megakernel…",
-// section "写在最后"; page "AI手搓1.2万行代码榨干GB300!…", section 03).
+// Between kernels data passes through stream order.  Inside a launch only
+// k3_down's chunk combine crosses workgroups, through agent-scope atomic
+// accesses and a counter (the ordering bug the pages report came from
+// activation loads moved above a wait: page "英伟达用1.2万行CuTe DSL
+// Megakernel…", section "写在最后"; page "AI手搓1.2万行代码榨干GB300!…",
+// section 03).
+#include "moe.h"
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "moe_topk.h"
@@ -142,12 +149,22 @@ __device__ __forceinline__ int x_chunk_pos(int b, int q) {
 struct XStage {
   uint4 v[kChunksPerLane];
 };
+// Every workgroup copies the same x at the same moment; each starts at its
+// own chunk (a rotation of the order), so that the workgroups of an XCD do
+// not all ask one L2 channel for the same lines.  Chunk slots past the end
+// of x hold the zero padding at their own positions.
+__device__ __forceinline__ int x_stage_chunk(int i, int nch) {
+  const int c = threadIdx.x + i * kBlock;
+  if (c >= nch) return c;
+  const int r = c + (int)(((unsigned)blockIdx.x * 8u * 8u) % (unsigned)nch);
+  return r >= nch ? r - nch : r;
+}
 __device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int H, XStage& st) {
   const uint4* x16 = reinterpret_cast<const uint4*>(x);
   const int nch = H / 8;
 #pragma unroll
   for (int i = 0; i < kChunksPerLane; ++i) {
-    const int c = threadIdx.x + i * kBlock;
+    const int c = x_stage_chunk(i, nch);
     st.v[i] = x16[c < nch ? c : nch - 1];
   }
 }
@@ -156,7 +173,7 @@ __device__ __forceinline__ void stage_x_store(const XStage& st, int H, uint32_t*
   const int nch = H / 8;
 #pragma unroll
   for (int i = 0; i < kChunksPerLane; ++i) {
-    const int c = threadIdx.x + i * kBlock;
+    const int c = x_stage_chunk(i, nch);
     l16[x_chunk_pos(c >> 2, c & 3)] = keep_or_zero(c < nch, st.v[i]);
   }
   __syncthreads();
@@ -216,7 +233,9 @@ struct GateUpJob {
   const int32_t* e_lds;  // expert of each routed slot, in LDS
   int H, F, k;
   int ns;                // shared tasks (0 without a shared expert)
-  float* act;            // [k + 1][F]: routed slots, then the shared expert
+  float* act;            // fp32 [k + 1][F]: routed slots, then the shared expert
+  uint16_t* act_hl;      // or bf16 [2][nslot][F]: leading parts, then remainders
+  int nslot;
 };
 
 // LANES > 0 fixes the lanes per row at compile time: the block offsets of a
@@ -308,7 +327,15 @@ struct GateUp {
       bool sh;
       int slot, j;
       locate(J, t, sh, slot, j);
-      J.act[(size_t)slot * J.F + j] = silu(acc) * up;
+      const float a = silu(acc) * up;
+      if (J.act_hl) {  // a = hi + lo to about 16 significant bits
+        const uint16_t hi = f32_to_bf16(a);
+        const float d = a - bf16_to_f32(hi);
+        J.act_hl[(size_t)slot * J.F + j] = hi;
+        J.act_hl[(size_t)(J.nslot + slot) * J.F + j] = f32_to_bf16(d == d ? d : 0.f);
+      } else {
+        J.act[(size_t)slot * J.F + j] = a;
+      }
     }
   }
 };
@@ -342,91 +369,6 @@ __device__ void gateup_tasks(const GateUp<BPL, LANES>& g, const GateUpJob& J, co
     g.finish(J, x_lds, t, ca, sa);
   }
 }
-
-// -------------------------------------------------------------------------
-// Down rows of one matrix D[H][F] against fp32 activations held in
-// registers; `lanes` lanes per row, BPL blocks per lane, 64/lanes rows per
-// load instruction.
-// LANES > 0 fixes the lane count at compile time (shifts and a constant
-// reduction width); LANES = 0 takes it at run time.
-template <int BPL, int LANES = 0>
-struct DownLanes {
-  int rig, col, lanes, rpw;
-  float ar[BPL][32];
-
-  __device__ void init_map(int lanes_) {
-    const int lane = threadIdx.x & 63;
-    lanes = LANES ? LANES : lanes_;
-    rig = lane / lanes;
-    col = lane % lanes;
-    rpw = kWave / lanes;
-  }
-  __device__ __forceinline__ float reduce(float v) const {
-    if (LANES) return group_sum_last_c<LANES ? LANES : 64>(v);
-    return group_sum_last(v, lanes);
-  }
-  // Pins the activations: the wait for their loads happens here, not
-  // inside a later loop (an empty asm that claims to modify the registers).
-  __device__ __forceinline__ void settle_act() {
-#pragma unroll
-    for (int i = 0; i < BPL; ++i)
-#pragma unroll
-      for (int q = 0; q < 32; ++q) asm volatile("" : "+v"(ar[i][q]));
-  }
-  __device__ void load_act(const float* a) {
-    const float4* a16 = reinterpret_cast<const float4*>(a);
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      const int b = col + lanes * i;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 v = a16[b * 8 + q];
-        ar[i][4 * q + 0] = v.x;
-        ar[i][4 * q + 1] = v.y;
-        ar[i][4 * q + 2] = v.z;
-        ar[i][4 * q + 3] = v.w;
-      }
-    }
-  }
-  // Rows row0 .. row0 + rpw - 1 (row0 uniform across the wave; this lane's
-  // row is row0 + rig).  Addresses are a wave-uniform base plus a 32-bit
-  // lane offset, which keeps one scalar base per load instead of a 64-bit
-  // vector address (many rows are in flight at once).
-  __device__ __forceinline__ void load_row(const uint8_t* codes, const uint8_t* scales, int F,
-                                           int row0, uint4 (&c)[BPL], uint32_t (&sc)[BPL]) const {
-    const uint8_t* cb = codes + (size_t)row0 * (F / 2);
-    const uint8_t* sb = scales + (size_t)row0 * (F / 32);
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      const uint32_t b = (uint32_t)(col + lanes * i);
-      c[i] = ld_stream16(cb + ((uint32_t)rig * (uint32_t)(F / 2) + b * 16u));
-      sc[i] = ld_stream_word_of(sb + (uint32_t)rig * (uint32_t)(F / 32), (int)b);
-    }
-  }
-  // The same rows of one matrix given as buffer descriptors (codes, scales):
-  // the row offset goes in a scalar register, the lane offset in one vector
-  // register shared by every row.
-  __device__ __forceinline__ void load_row_buf(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
-                                               int F, int row0, uint4 (&c)[BPL],
-                                               uint32_t (&sc)[BPL]) const {
-    const uint32_t soc = (uint32_t)row0 * (uint32_t)(F / 2);
-    const uint32_t sos = (uint32_t)row0 * (uint32_t)(F / 32);
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      const uint32_t b = (uint32_t)(col + lanes * i);
-      c[i] = buf_ld16(rc, (uint32_t)rig * (uint32_t)(F / 2) + b * 16u, soc);
-      sc[i] = buf_ld4(rs, ((uint32_t)rig * (uint32_t)(F / 32) + b) & ~3u, sos);
-    }
-  }
-  __device__ __forceinline__ float dot(const uint4 (&c)[BPL], const uint32_t (&sc)[BPL]) const {
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < BPL; ++i)
-      acc = __builtin_fmaf(block_dot_f32(c[i], ar[i]),
-                           e8m0_to_f32(byte_of(sc[i], (col + lanes * i) & 3)), acc);
-    return acc;
-  }
-};
 
 // -------------------------------------------------------------------------
 // K1a: router rows.  Each wave requests its first row before x is staged
@@ -481,7 +423,8 @@ __global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, 
   const int wid = wave_id();
   const GateUpJob J{L.g_codes,  L.g_scales,  L.u_codes,  L.u_scales, L.sg_codes, L.sg_scales,
                     L.su_codes, L.su_scales, e_lds,      L.H,        L.F,        L.k,
-                    ns,         act};
+                    ns,         act,        act ? nullptr : L.act_hl,
+                    L.k + (L.S ? 1 : 0)};
   GateUp<BPLH, LANES> g;
   g.init(J, gu_lanes);
   const int first = blockIdx.x * kWaves + wid, ntask = ns + L.k * g.tps;
@@ -526,407 +469,368 @@ __global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, 
   gateup_tasks(g, J, x_lds, ntask, first, gridDim.x * kWaves, ca, sa);
 }
 
-// K3: one workgroup per row slab of `gpb` row groups, one slab per CU.  With
-// nw waves, wave w streams the slab's rows of two routed slots at once, w
-// and w + nw (then w + 2 nw and w + 3 nw, ...), with the activations of
-// both slots in registers.  Rows go in bursts of kK3Burst row groups per
-// slot, double-buffered: the next burst is requested before the current one
-// is reduced, so every wave keeps one to two bursts in flight.  A wave left
-// with a single slot streams that slot alone.  The shared expert (weight 1)
-// is split by rows instead: wave w takes its share of the slab's rows.  Its
-// rows and activations need no routing, so they are requested first, while
-// the expert ids are still in flight, and reduced once the first routed
-// burst has been requested.  Each row result is added to the wave's own LDS
-// partial; the partials are then summed in wave order and the residual is
-// added.  (F = 4096 keeps one routed slot per pass: its two blocks per lane
-// double the activation registers.)
-constexpr int kK3MaxWaves = 8;  // 2 waves per SIMD: up to 256 registers
-constexpr int kK3MaxRows = 64;
-constexpr int kK3Burst = 4;
-constexpr int kK3ShRows = 4;     // shared row groups requested up front per wave
+// K3: down projection of every slot on the matrix cores, router-weighted
+// combine with the shared expert (weight 1) and residual add -> bf16.
+//
+// Workgroup (slot s, chunk c): the chunk is a run of row groups of the
+// slot's down matrix D[H][F], and the workgroup's waves are kqn slices of
+// the reduction index (NI load instructions each) times nsn row streams.
+// One load instruction reads 64 / CPR rows, 16 CPR contiguous bytes of each
+// (four rows x 256 bytes when F >= 512: whole cache lines), one MXFP4 block
+// per lane.  The lanes are laid out as v_mfma_f32_4x4x4_16b_bf16 wants them:
+// lane 4 b + i holds A_b[i][.] (row i of block b, b = one lane's block) and
+// B_b[.][i] (column i), so the loaded blocks are A operands as they stand.
+// Block b's B operand is the matching stretch of the slot's activation:
+// column 0 its leading bf16 part, column 1 the remainder (together about 16
+// significant bits), columns 2 and 3 zero.  A wave holds its slice of B for
+// the whole launch; the vector ALU only decodes codes to exact bf16 (scale
+// folded in), the matrix cores multiply, and each row's total is the sum of
+// its accumulator over the lanes of its blocks.  Every wave keeps three row
+// groups' loads in flight.  Slice sums meet in LDS, added in slice order.
+//
+// The combine crosses workgroups: the nslots workgroups of a chunk store
+// their weighted rows with agent-scope atomic stores (coherent across the
+// L2s), wait until the stores have completed and then count themselves on
+// the chunk's counter.  The workgroup that counts last reads every slot's
+// rows with agent-scope atomic loads, sums them in slot order
+// (deterministic: no floating-point atomics), adds the residual, stores bf16
+// and clears the counter for the next call.  Only these coherent accesses
+// cross workgroups, so no cache writeback or invalidate is needed.
+constexpr int kK3W = 8;                       // waves per workgroup (two per SIMD)
+// row groups in flight per wave, within 256 registers (two waves per SIMD)
+constexpr int k3_depth(int ni) { return ni == 4 ? 4 : 6; }
+constexpr int kK3RedFloats = 8192;            // LDS slice sums [kqn][chunk rows]
+constexpr int kK3MaxChunks = MOE_WS_COUNTER_BYTES / 4;
 
-template <int BPLF, int LANES>
-struct DownBurst {
-  uint4 ca[kK3Burst][BPLF], cb[kK3Burst][BPLF];
-  uint32_t xa[kK3Burst][BPLF], xb[kK3Burst][BPLF];
+typedef __attribute__((ext_vector_type(4))) short s16x4;  // four bf16: a 4x4x4 operand
+
+template <int NI>
+struct DownGroup {
+  uint4 c[NI];      // per instruction: this lane's MXFP4 block (16 code bytes)
+  uint32_t sc[NI];  // per instruction: the row's scale dword holding the block's byte
 };
 
-// Where a slot's down rows come from: buffer descriptors of its matrix, its
-// combine weight and its activations.
-struct DownSlot {
-  __amdgpu_buffer_rsrc_t rc, rs;
-  float w;
-  const float* act;
-};
-// Routed slot s (< k).  e_v / w_v hold the routed experts and weights one
-// per lane (lane i: slot i), loaded once by the caller, so that every slot
-// reads them with a lane read instead of a memory round trip of its own.
-__device__ __forceinline__ DownSlot routed_slot(const LayerT1& L, int s, int e_v, float w_v) {
-  const size_t mat_c = (size_t)L.H * (L.F / 2), mat_s = (size_t)L.H * (L.F / 32);
-  const int e0 = __builtin_amdgcn_readlane(e_v, s);
-  const int e = e0 < 0 ? 0 : (e0 >= L.E ? L.E - 1 : e0);  // never address outside
-  DownSlot d;
-  d.rc = buf_rsrc(L.d_codes + e * mat_c, (uint32_t)mat_c);
-  d.rs = buf_rsrc(L.d_scales + e * mat_s, (uint32_t)mat_s);
-  d.w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_v), s));
-  d.act = L.act + (size_t)s * L.F;
-  return d;
+__device__ __forceinline__ s16x4 pack_bf16x4(bf16x2 lo, bf16x2 hi) {
+  const uint2 v = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+  return __builtin_bit_cast(s16x4, v);
 }
-// The shared expert; without one the descriptors are empty (reads give 0)
-// and the activations point at slot 0 (in bounds, unused).
-__device__ __forceinline__ DownSlot shared_slot(const LayerT1& L) {
-  const size_t mat_c = (size_t)L.H * (L.F / 2), mat_s = (size_t)L.H * (L.F / 32);
-  DownSlot d;
-  d.rc = buf_rsrc(L.S ? L.sd_codes : nullptr, L.S ? (uint32_t)mat_c : 0u);
-  d.rs = buf_rsrc(L.S ? L.sd_scales : nullptr, L.S ? (uint32_t)mat_s : 0u);
-  d.w = 1.f;
-  d.act = L.act + (L.S ? (size_t)L.k * L.F : 0);
-  return d;
+__device__ __forceinline__ s16x4 dwords_bf16x4(uint32_t a, uint32_t b) {
+  const uint2 v = make_uint2(a, b);
+  return __builtin_bit_cast(s16x4, v);
+}
+__device__ __forceinline__ f32x4 mfma4(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// One wave's pass over the slab for one or two routed slots (TWO),
-// accumulating into its LDS partial row `red`; `between` runs once the
-// first bursts and the activations have been requested.  DEPTH bursts are
-// in flight while one is reduced.  Every request is unconditional: a load
-// under a branch that rejoins makes the compiler wait for the newer loads
-// as well.  Bursts past the slab end are issued against an empty
-// descriptor: they return zeros without a memory access (a scalar select,
-// so the lane offsets stay loop-invariant registers).
-template <int BPLF, int LANES, bool TWO, int DEPTH, typename Between>
-__device__ __forceinline__ void down_pass(const LayerT1& L, const DownSlot& A, const DownSlot& B,
-                                          DownLanes<BPLF, LANES>& dA, DownLanes<BPLF, LANES>& dB,
-                                          int gbase, int ng, float* red, Between between) {
-  constexpr int NB = kK3Burst;
-  const int nb = (ng + NB - 1) / NB;
-  const __amdgpu_buffer_rsrc_t none = buf_rsrc(nullptr, 0u);
-  auto load_burst = [&](int i, DownBurst<BPLF, LANES>& P) {
-    const bool skip = i >= nb;
-    const auto rca = skip ? none : A.rc, rsa = skip ? none : A.rs;
-    const auto rcb = skip ? none : B.rc, rsb = skip ? none : B.rs;
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One row group on the matrix cores.  Lane 4 b + i4 holds, for each of the
+// NI instructions, block cc of row 4 rho + i4 (codes and scale dword) and
+// the matching B fragments (bv: 32 bf16 of the activation, column i4).
+// Returns the row quad's four row sums, valid in the quad's last lane.
+template <int CPR, int NI>
+__device__ __forceinline__ f32x4 down_group_rows(const DownGroup<NI>& P, const u32x4 (&bv)[NI][4], int cc) {
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int g = i * NB + j;
-      const int row0 = (gbase + (g < ng ? g : ng - 1)) * dA.rpw;
-      dA.load_row_buf(rca, rsa, L.F, row0, P.ca[j], P.xa[j]);
-      if (TWO) dB.load_row_buf(rcb, rsb, L.F, row0, P.cb[j], P.xb[j]);
-    }
-  };
-  auto use_burst = [&](int i, const DownBurst<BPLF, LANES>& P) {
-    const int g0 = i * NB;
-    float v[NB];
+  for (int t = 0; t < NI; ++t) {
+    const float scl = e8m0_to_f32(byte_of(P.sc[t], cc & 3));
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      // one row of one slot at a time: unpacking more at once costs registers
-      v[j] = A.w * dA.dot(P.ca[j], P.xa[j]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (TWO) v[j] = __builtin_fmaf(B.w, dB.dot(P.cb[j], P.xb[j]), v[j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) v[j] = dA.reduce(v[j]);
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      if (g0 + j < ng && dA.col == dA.lanes - 1) red[(g0 + j) * dA.rpw + dA.rig] += v[j];
-  };
-  // Activations first: the loop is then entered, as it is re-entered, with
-  // exactly the weight bursts outstanding, and the compiler's wait counts
-  // in the loop need not cover a younger activation load.
-  dA.load_act(A.act);
-  if (TWO) dB.load_act(B.act);
-  DownBurst<BPLF, LANES> P, Q;
-  load_burst(0, P);
-  if constexpr (DEPTH == 3) {
-    DownBurst<BPLF, LANES> R;
-    load_burst(1, Q);
-    // Wait for the activations now, with two bursts in flight: entering the
-    // loop with them still outstanding would put 64 loads in flight at its
-    // first request, past what the wait counter tracks, and every later
-    // wait in the loop would be too deep.
-    dA.settle_act();
-    if (TWO) dB.settle_act();
-    between();
-    for (int i = 0; i < nb; i += 3) {
-      load_burst(i + 2, R);
-      __builtin_amdgcn_sched_barrier(0);
-      use_burst(i, P);
-      if (i + 1 >= nb) break;
-      load_burst(i + 3, P);
-      __builtin_amdgcn_sched_barrier(0);
-      use_burst(i + 1, Q);
-      if (i + 2 >= nb) break;
-      load_burst(i + 4, Q);
-      __builtin_amdgcn_sched_barrier(0);
-      use_burst(i + 2, R);
-    }
-  } else {
-    between();
-    for (int i = 0; i < nb; i += 2) {
-      load_burst(i + 1, Q);
-      __builtin_amdgcn_sched_barrier(0);
-      use_burst(i, P);
-      if (i + 1 >= nb) break;
-      load_burst(i + 2, P);
-      __builtin_amdgcn_sched_barrier(0);
-      use_burst(i + 1, Q);
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t cw = dword_of(P.c[t], u);
+      const s16x4 x0 = pack_bf16x4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scl, 0),
+                                   __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scl, 1));
+      const s16x4 x1 = pack_bf16x4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scl, 2),
+                                   __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scl, 3));
+      a0 = mfma4(x0, dwords_bf16x4(bv[t][u][0], bv[t][u][1]), a0);
+      a1 = mfma4(x1, dwords_bf16x4(bv[t][u][2], bv[t][u][3]), a1);
     }
   }
+  // row 4 rho + r: accumulator r summed over the row quad's lanes
+  f32x4 v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = group_sum_last_c<4 * CPR>(a0[r] + a1[r]);
+  return v;
 }
 
-template <int BPLF, int LANES>
-__global__ __launch_bounds__(kK3MaxWaves * kWave) void k3_down_combine(LayerT1 L, int dn_lanes,
-                                                                       int gpb) {
-  __shared__ float red[kK3MaxWaves][kK3MaxRows];
-  constexpr bool PAIRS = BPLF == 1;
+template <int CPR, int NI, int D, int W>
+__global__ __launch_bounds__(W * kWave) void k3_down(LayerT1 L, int nchunk,
+                                                                                    int kqn, int nsn) {
+  constexpr int RPI = 64 / CPR;  // rows of a row group
+  constexpr int GW = 4 * CPR;    // lanes of one row quad
+  __shared__ __align__(16) float red[kK3RedFloats];
+  __shared__ int last;
   const int wid = wave_id(), lane = threadIdx.x & 63;
-  const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
-  // routed experts and weights, lane i holding slot i (k <= 32 < 64); these
-  // go first so that waiting for them leaves the later requests in flight
-  const int e_v = L.idx[lane < L.k ? lane : 0];
-  const float w_v = L.wts[lane < L.k ? lane : 0];
-  DownLanes<BPLF, LANES> dA, dB, dS;
-  dA.init_map(dn_lanes);
-  dB.init_map(dn_lanes);
-  dS.init_map(dn_lanes);
-  const int ngroups = L.H / dA.rpw;
-  const int gbase = blockIdx.x * gpb;
-  const int ng = ngroups - gbase < gpb ? ngroups - gbase : gpb;  // groups of this slab
-  const int R = ng * dA.rpw;
-  // each wave zeroes and later accumulates only its own partial row: no
-  // barrier needed before the first accumulation
-  for (int t = lane; t < R; t += kWave) red[wid][t] = 0.f;
-  // residual of this thread's output row, requested now so that the final
-  // combine waits on nothing but LDS.  A raw 32-bit buffer read: without a
-  // residual the descriptor is empty and the read gives 0, with no branch.
-  const int trow = gbase * dA.rpw + (threadIdx.x < R ? threadIdx.x : 0);
-  const uint32_t res_word = buf_ld4(buf_rsrc(L.residual, L.residual ? (uint32_t)L.H * 2u : 0u),
-                                    ((uint32_t)trow * 2u) & ~3u, 0u);
-  // this wave's share of the shared expert's row groups: [sh0, sh1)
-  const int sh0 = L.S ? wid * ng / nw : 0, sh1 = L.S ? (wid + 1) * ng / nw : 0;
-  const DownSlot SH = shared_slot(L);
-  uint4 shc[kK3ShRows][BPLF];
-  uint32_t shs[kK3ShRows][BPLF];
-#pragma unroll
-  for (int j = 0; j < kK3ShRows; ++j) {
-    const int g = sh0 + j < sh1 ? sh0 + j : (sh1 > sh0 ? sh1 - 1 : 0);
-    dS.load_row_buf(SH.rc, SH.rs, L.F, (gbase + g) * dS.rpw, shc[j], shs[j]);
-  }
-  dS.load_act(SH.act);
-  auto shared_rows = [&]() {
-#pragma unroll
-    for (int j = 0; j < kK3ShRows; ++j) {
-      float v = dS.dot(shc[j], shs[j]);
-      __builtin_amdgcn_sched_barrier(0);
-      v = dS.reduce(v);
-      if (sh0 + j < sh1 && dS.col == dS.lanes - 1) red[wid][(sh0 + j) * dS.rpw + dS.rig] += v;
-    }
-  };
-
-  const int step = PAIRS ? 2 * nw : nw;
-  auto routed = [&](int s0, auto between) {
-    const int sb = s0 + nw;
-    const DownSlot A = routed_slot(L, s0, e_v, w_v);
-    // three bursts in flight where the registers allow it (one block per lane)
-    constexpr int DEPTH = BPLF == 1 ? 3 : 2;
-    if (PAIRS && sb < L.k) {
-      const DownSlot B = routed_slot(L, sb, e_v, w_v);
-      down_pass<BPLF, LANES, PAIRS, DEPTH>(L, A, B, dA, dB, gbase, ng, red[wid], between);
-    } else {
-      down_pass<BPLF, LANES, false, DEPTH>(L, A, A, dA, dB, gbase, ng, red[wid], between);
-    }
-  };
-  // The first pass is not part of the loop: inside it the shared rows would
-  // be loop-invariant, and the compiler would reduce them (and wait for
-  // them) before the first routed burst is requested.
-  if (wid < L.k) {
-    routed(wid, [&]() {
-      __builtin_amdgcn_sched_barrier(0);
-      shared_rows();
-    });
-  } else {
-    shared_rows();  // a wave without routed slots
-  }
-  for (int s0 = wid + step; s0 < L.k; s0 += step) routed(s0, []() {});
-  // shared row groups past the ones requested up front (only when the slab
-  // has more than kK3ShRows groups per wave)
-  for (int g = sh0 + kK3ShRows; g < sh1; ++g) {
-    uint4 c[BPLF];
-    uint32_t x[BPLF];
-    dS.load_row_buf(SH.rc, SH.rs, L.F, (gbase + g) * dS.rpw, c, x);
-    const float v = dS.reduce(dS.dot(c, x));
-    if (dS.col == dS.lanes - 1) red[wid][g * dS.rpw + dS.rig] += v;
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < R) {  // R <= kK3MaxRows <= the workgroup size
-    float tot = 0.f;
-    for (int v = 0; v < nw; ++v) tot += red[v][threadIdx.x];
-    const float res = bf16_to_f32((res_word >> (16 * (trow & 1))) & 0xFFFFu);
-    const uint16_t o = f32_to_bf16(tot + res);
-    L.out[trow] = o;
-    if (L.trace) L.trace[trow] = o;
-  }
-}
-
-// K3, activations in LDS (one block per lane, F a multiple of 32 x lanes,
-// and every slot's activations within kK3LdsActBytes).  The workgroup first
-// copies the activations of all slots into LDS; then the work is a list of
-// bursts, (slot, kK3Burst row groups of the slab), the shared expert's
-// first, dealt round robin to kK3LdsWaves waves.  A wave keeps three bursts
-// in flight and reads the slot's activations from LDS once per burst, so it
-// needs few registers: four waves per SIMD.  Requests past the end of a
-// wave's list go to an empty descriptor (zeros, no memory traffic).  Row
-// results go to the wave's LDS partial row; partials are summed in wave
-// order with the residual, as in the register variant.
-constexpr int kK3LdsWaves = 16;
-constexpr int kK3LdsActBytes = 144 * 1024;
-static_assert(kK3LdsActBytes % (16 * kK3LdsWaves * kWave) == 0, "whole staging rounds");
-
-template <int LANES>
-struct LdsBurst {
-  uint4 c[kK3Burst];
-  uint32_t x[kK3Burst];
-  int as, c0;  // activation slot and first row group (wave-uniform)
-  float w;     // combine weight
-};
-
-template <int LANES>
-__global__ __launch_bounds__(kK3LdsWaves * kWave) void k3_down_lds(LayerT1 L, int gpb) {
-  extern __shared__ __align__(16) float k3_smem[];
-  float* act_lds = k3_smem;                                        // [slots][8][F/32][4]
-  float* red = k3_smem + (size_t)(L.k + (L.S ? 1 : 0)) * L.F;   // [waves][kK3MaxRows]
-  constexpr int NB = kK3Burst;
-  // one block per lane: F = 32 LANES, and a row group (64 / LANES rows) is
-  // always 1 KB of codes and 64 bytes of scales
-  constexpr uint32_t kGroupCodes = 1024, kGroupScales = 64;
-  const int wid = wave_id(), lane = threadIdx.x & 63;
+  const int b = lane >> 2, i4 = lane & 3;       // MFMA block; row (A) and column (B) in it
+  const int rho = b / CPR, cc = b - rho * CPR;  // row quad, block within the instruction
   const int nslots = L.k + (L.S ? 1 : 0);
-  // routed experts and weights, lane i holding slot i (k <= 32 < 64)
-  const int e_v = L.idx[lane < L.k ? lane : 0];
-  const float w_v = L.wts[lane < L.k ? lane : 0];
-  DownLanes<1, LANES> d;
-  d.init_map(LANES);
-  const int ngroups = L.H / d.rpw;
-  const int gbase = blockIdx.x * gpb;
-  const int ng = ngroups - gbase < gpb ? ngroups - gbase : gpb;  // groups of this slab
-  const int R = ng * d.rpw;
-  float* red_w = red + wid * kK3MaxRows;
-  for (int t = lane; t < R; t += kWave) red_w[t] = 0.f;
-  const int trow = gbase * d.rpw + (threadIdx.x < R ? threadIdx.x : 0);
-  const uint32_t res_word = buf_ld4(buf_rsrc(L.residual, L.residual ? (uint32_t)L.H * 2u : 0u),
-                                    ((uint32_t)trow * 2u) & ~3u, 0u);
-  // activations -> LDS: float4 j of a slot (elements 4j..4j+3, block j/8,
-  // chunk j%8) goes to position (j%8) * nbk + j/8, so that a chunk read of
-  // consecutive blocks by consecutive lanes touches consecutive addresses
-  const int nbk = L.F / 32, f4_per_slot = L.F / 4, f4_total = nslots * f4_per_slot;
-  // one staging round covers kK3LdsActBytes (the launcher's bound)
-  constexpr int kStage = kK3LdsActBytes / 16 / (kK3LdsWaves * kWave);
-  f32x4 st[kStage];  // native vectors: an array of HIP's float4 struct lands in scratch
+  const int s = blockIdx.x / nchunk, c = blockIdx.x - s * nchunk;  // slot, chunk
+  const int kq = wid % kqn, st = wid / kqn;                        // slice, row stream
+  const int nrg = L.H / RPI, nb = L.F / 32;
+  const int cg0 = c * nrg / nchunk, cg1 = (c + 1) * nrg / nchunk;  // the chunk's row groups
+  const int crows = (cg1 - cg0) * RPI;
+  const int g0 = cg0 + (cg1 - cg0) * st / nsn, g1 = cg0 + (cg1 - cg0) * (st + 1) / nsn;
+  const int n = g1 - g0;  // row groups of this wave
+  // the slot: routed (expert idx[s], weight wts[s]) or, s == k, the shared one
+  const bool sh = s >= L.k;
+  const int e0 = sh ? 0 : L.idx[s];
+  const int e = sh ? 0 : (e0 < 0 ? 0 : (e0 >= L.E ? L.E - 1 : e0));  // never address outside
+  const float w = sh ? 1.f : L.wts[s];
+  const uint32_t F2 = (uint32_t)L.F / 2, F32 = (uint32_t)L.F / 32;
+  const uint32_t mat_c = (uint32_t)L.H * F2, mat_s = (uint32_t)L.H * F32;
+  const uint8_t* cb = (sh ? L.sd_codes : L.d_codes) + (size_t)e * mat_c;
+  const uint8_t* sb = (sh ? L.sd_scales : L.d_scales) + (size_t)e * mat_s;
+  const uint32_t row_in = 4u * (uint32_t)rho + (uint32_t)i4;  // this lane's row in a group (A)
+  // instruction t reads block (kq NI + t) CPR + cc of each row; blocks past
+  // the row (F / 32 not a multiple of CPR) re-read the row's last block and
+  // meet a zero B operand; instructions wholly past it are not issued
+  // (empty descriptor)
+  uint32_t voc[NI], vos[NI], voa[NI];
+  bool ilive[NI];
+  {
+    const uint32_t arow = (uint32_t)((i4 == 1 ? nslots + s : s) * L.F);
 #pragma unroll
-  for (int u = 0; u < kStage; ++u) {
-    const int j = u * (int)blockDim.x + (int)threadIdx.x;
-    st[u] = reinterpret_cast<const f32x4*>(L.act)[j < f4_total ? j : f4_total - 1];
+    for (int t = 0; t < NI; ++t) {
+      const int gb = (kq * NI + t) * CPR + cc;
+      const int gbc = gb < nb ? gb : nb - 1;
+      ilive[t] = (kq * NI + t) * CPR < nb;
+      voc[t] = row_in * F2 + 16u * (uint32_t)gbc;
+      vos[t] = row_in * F32 + 4u * (uint32_t)(gbc >> 2);
+      voa[t] = (gb < nb && i4 < 2) ? 2u * (arow + 32u * (uint32_t)gb) : 0xFFFFFF00u;
+    }
   }
-
-  // this wave's bursts: b = wid, wid + nw, ...; burst b covers list slot
-  // p = b / nch (0: the shared expert when present) and chunk b % nch
-  const int nch = (ng + NB - 1) / NB, nbt = nslots * nch;
-  constexpr int nw = kK3LdsWaves;
-  // b / nch as a multiply and shift (scalar divisions are long sequences):
-  // exact for b < 2^16 / 64 with nch <= 64 (here b < 33 * 16, nch <= 16)
-  const int inv_nch = (65536 + nch - 1) / nch;
-  const size_t mat_c = (size_t)L.H * (L.F / 2), mat_s = (size_t)L.H * (L.F / 32);
-  // lane offsets within a row group (loop-invariant vector registers)
-  const uint32_t voc = (uint32_t)d.rig * (uint32_t)(L.F / 2) + (uint32_t)d.col * 16u;
-  const uint32_t vos = ((uint32_t)d.rig * (uint32_t)(L.F / 32) + (uint32_t)d.col) & ~3u;
-  // Burst i of this wave: slot, weight and row groups are computed once,
-  // here, and travel with the buffer.  The matrix base and the size are
-  // selected as scalars and one descriptor is built from them (selecting
-  // whole descriptors compiles to branches).  Row groups past the slab end
-  // read the next rows of the matrix, or zeros past its end; their results
-  // are dropped.
-  auto load_burst = [&](int i, LdsBurst<LANES>& P) {
-    const int b = wid + i * nw;
-    const int bb = b < nbt ? b : nbt - 1;
-    const int p = (bb * inv_nch) >> 16;
-    const bool sh = L.S && p == 0;
-    const int s = sh ? 0 : p - (L.S ? 1 : 0);  // routed slot
-    const int e0 = __builtin_amdgcn_readlane(e_v, s);
-    const int e = sh ? 0 : (e0 < 0 ? 0 : (e0 >= L.E ? L.E - 1 : e0));  // never address outside
-    P.as = sh ? L.k : s;
-    P.w = sh ? 1.f : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_v), s));
-    P.c0 = (bb - p * nch) * NB;
-    const bool live = b < nbt;
-    const auto rc = buf_rsrc((sh ? L.sd_codes : L.d_codes) + (size_t)e * mat_c,
-                             live ? (uint32_t)mat_c : 0u);
-    const auto rs = buf_rsrc((sh ? L.sd_scales : L.d_scales) + (size_t)e * mat_s,
-                             live ? (uint32_t)mat_s : 0u);
-    const uint32_t g0 = (uint32_t)(gbase + P.c0);
+  // B operand: the block's 32 activation elements (column i4), or zeros
+  u32x4 bv[NI][4];
+  {
+    const auto ra = buf_rsrc(L.act_hl, 4u * (uint32_t)nslots * (uint32_t)L.F);  // [2][nslots][F] bf16
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      P.c[j] = buf_ld16(rc, voc + j * kGroupCodes, g0 * kGroupCodes);
-      P.x[j] = buf_ld4(rs, vos + j * kGroupScales, g0 * kGroupScales);
+    for (int t = 0; t < NI; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        bv[t][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 ra, (int)(voa[t] + 16u * u), 0, kBufNT));
+  }
+  auto load_group = [&](int i, DownGroup<NI>& P) {
+    const bool live = i < n;
+    const uint32_t g = (uint32_t)__builtin_amdgcn_readfirstlane(g0 + (live ? i : 0));
+    const uint32_t soc = g * RPI * F2, sos = g * RPI * F32;
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const bool lv = live && ilive[t];
+      P.c[t] = buf_ld16(buf_rsrc(cb, lv ? mat_c : 0u), voc[t], soc);
+      P.sc[t] = buf_ld4(buf_rsrc(sb, lv ? mat_s : 0u), vos[t], sos);
     }
   };
-  auto use_burst = [&](int i, const LdsBurst<LANES>& P) {
-    const bool live = wid + i * nw < nbt;
-    // this lane's 32 activations of the slot, chunk by chunk
-    const f32x4* a4 = reinterpret_cast<const f32x4*>(act_lds) + (size_t)P.as * f4_per_slot + d.col;
+  auto use_group = [&](int i, const DownGroup<NI>& P) {
+    const f32x4 v = down_group_rows<CPR, NI>(P, bv, cc);
+    if ((lane & (GW - 1)) == GW - 1)
+      *reinterpret_cast<f32x4*>(&red[kq * crows + (g0 + i - cg0) * RPI + 4 * rho]) = v;
+  };
+  // issue order is wait order: activation, then groups 0 .. D-2 (pinned).
+  // The activation is waited for here, with those groups in flight, so that
+  // the loop is entered as it is re-entered: with D - 1 groups pending
+  DownGroup<NI> ring[D];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const f32x4 v = a4[q * nbk];
-      d.ar[0][4 * q + 0] = v.x;
-      d.ar[0][4 * q + 1] = v.y;
-      d.ar[0][4 * q + 2] = v.z;
-      d.ar[0][4 * q + 3] = v.w;
-    }
-    float v[NB];
+  for (int k = 0; k < D - 1; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_group(k, ring[k]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const uint4 c1[1] = {P.c[j]};
-      const uint32_t x1[1] = {P.x[j]};
-      v[j] = P.w * d.dot(c1, x1);
+  for (int t = 0; t < NI; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(bv[t][u]));
+  // whole rounds of D groups (group i + k + D - 1 requested before group
+  // i + k is used), then the last D - 1 at most
+  int i = 0;
+  for (; i + D <= n; i += D) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      load_group(i + k + D - 1, ring[(k + D - 1) % D]);
       __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) v[j] = d.reduce(v[j]);
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      if (live && P.c0 + j < ng && d.col == d.lanes - 1) red_w[(P.c0 + j) * d.rpw + d.rig] += v[j];
-  };
-
-  LdsBurst<LANES> P, Q, Rb;
-  load_burst(0, P);
-  load_burst(1, Q);
-#pragma unroll
-  for (int u = 0; u < kStage; ++u) {
-    const int j = u * (int)blockDim.x + (int)threadIdx.x;
-    if (j < f4_total) {
-      const int sl = j / f4_per_slot, jj = j - sl * f4_per_slot;
-      reinterpret_cast<f32x4*>(act_lds)[sl * f4_per_slot + (jj & 7) * nbk + (jj >> 3)] = st[u];
+      use_group(i + k, ring[k]);
     }
   }
-  __syncthreads();  // activations in LDS
-  const int nb = (nbt - wid + nw - 1) / nw;  // bursts of this wave
-  for (int i = 0; i < nb; i += 3) {
-    load_burst(i + 2, Rb);
-    __builtin_amdgcn_sched_barrier(0);
-    use_burst(i, P);
-    if (i + 1 >= nb) break;
-    load_burst(i + 3, P);
-    __builtin_amdgcn_sched_barrier(0);
-    use_burst(i + 1, Q);
-    if (i + 2 >= nb) break;
-    load_burst(i + 4, Q);
-    __builtin_amdgcn_sched_barrier(0);
-    use_burst(i + 2, Rb);
-  }
+#pragma unroll
+  for (int k = 0; k < D - 1; ++k)
+    if (i + k < n) use_group(i + k, ring[k]);
   __syncthreads();
-  if ((int)threadIdx.x < R) {  // R <= kK3MaxRows <= the workgroup size
+
+  // the slot's weighted rows of the chunk (slices in order), published
+  float* part = L.part + (size_t)s * L.H + (size_t)cg0 * RPI;
+  for (int r = (int)threadIdx.x; r < crows; r += (int)blockDim.x) {
+    float v = 0.f;
+    for (int kk = 0; kk < kqn; ++kk) v += red[kk * crows + r];
+    st_agent(part + r, w * v);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(&L.counters[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (uint32_t)(nslots - 1);
+  __syncthreads();
+  if (!last) return;
+  // last of the chunk: every slot's rows, summed in slot order (all requested
+  // at once; indices past the last slot repeat it and are masked)
+  const float* p0 = L.part + (size_t)cg0 * RPI;
+  for (int r = (int)threadIdx.x; r < crows; r += (int)blockDim.x) {
+    float pv[kMaxTopK + 1];
+#pragma unroll
+    for (int u = 0; u <= kMaxTopK; ++u) pv[u] = ld_agent(p0 + (size_t)(u < nslots ? u : nslots - 1) * L.H + r);
     float tot = 0.f;
-    for (int v = 0; v < nw; ++v) tot += red[v * kK3MaxRows + threadIdx.x];
-    const float res = bf16_to_f32((res_word >> (16 * (trow & 1))) & 0xFFFFu);
-    const uint16_t o = f32_to_bf16(tot + res);
-    L.out[trow] = o;
-    if (L.trace) L.trace[trow] = o;
+#pragma unroll
+    for (int u = 0; u <= kMaxTopK; ++u) tot += u < nslots ? pv[u] : 0.f;
+    const int row = cg0 * RPI + r;
+    if (L.residual) tot += bf16_to_f32(L.residual[row]);
+    const uint16_t o = f32_to_bf16(tot);
+    L.out[row] = o;
+    if (L.trace) L.trace[row] = o;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&L.counters[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// K3 when the split activations of every slot fit in LDS (F <= 2048 with
+// these tiles): workgroup = a slab of gpb row groups for every slot, so the
+// slots are combined inside the workgroup and no workgroup waits for
+// another.  The activations ([2][nslots][F] bf16) are copied to LDS with
+// direct loads issued before the first weight requests (waiting for them
+// then leaves the weights in flight).  A wave's tasks are consecutive
+// (slot, row group) pairs in slot-major order, so it reads its B operand
+// from LDS only when its slot changes.  The weighted row sums of every slot
+// meet in LDS and are added in slot order, with the residual.
+constexpr int kK3SlabW = 8;                  // waves per workgroup (two per SIMD)
+constexpr int kK3SlabD = 4;                  // row groups in flight per wave
+constexpr size_t kK3SlabLds = 156 * 1024;    // LDS budget: activations + row sums
+
+template <int CPR, int NI>
+__global__ __launch_bounds__(kK3SlabW * kWave) void k3_slab(LayerT1 L, int gpb) {
+  constexpr int RPI = 64 / CPR, GW = 4 * CPR, D = kK3SlabD, W = kK3SlabW;
+  extern __shared__ __align__(16) uint8_t k3_smem[];
+  const int wid = wave_id(), lane = threadIdx.x & 63;
+  const int b = lane >> 2, i4 = lane & 3;       // MFMA block; row (A) and column (B) in it
+  const int rho = b / CPR, cc = b - rho * CPR;  // row quad, block within the instruction
+  const int nslots = L.k + (L.S ? 1 : 0);
+  const int nrg = L.H / RPI, nb = L.F / 32;
+  const int gb0 = blockIdx.x * gpb;
+  const int G = gpb < nrg - gb0 ? gpb : nrg - gb0;  // row groups of this workgroup
+  const int srows = G * RPI;
+  const int ntask = nslots * G;
+  const int w0 = ntask * wid / W, n = ntask * (wid + 1) / W - w0;  // this wave's tasks
+  const uint32_t abytes = 4u * (uint32_t)nslots * (uint32_t)L.F;
+  const uint32_t akb = (abytes + 1023u) / 1024u;  // 1 KB copies
+  float* red = reinterpret_cast<float*>(k3_smem + 1024u * akb);  // [nslots][srows]
+
+  // activations -> LDS, one KB per wave instruction (past the end: zeros)
+  {
+    const auto ra = buf_rsrc(L.act_hl, abytes);
+    for (uint32_t kb = (uint32_t)wid; kb < akb; kb += W)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, k3_smem + 1024u * kb, 16, 16 * lane, 1024 * kb, 0, 0);
+  }
+  const uint32_t F2 = (uint32_t)L.F / 2, F32 = (uint32_t)L.F / 32;
+  const uint32_t mat_c = (uint32_t)L.H * F2, mat_s = (uint32_t)L.H * F32;
+  const uint32_t row_in = 4u * (uint32_t)rho + (uint32_t)i4;
+  uint32_t voc[NI], vos[NI];
+  bool ilive[NI];
+#pragma unroll
+  for (int t = 0; t < NI; ++t) {
+    const int gb = t * CPR + cc;
+    const int gbc = gb < nb ? gb : nb - 1;
+    ilive[t] = t * CPR < nb;
+    voc[t] = row_in * F2 + 16u * (uint32_t)gbc;
+    vos[t] = row_in * F32 + 4u * (uint32_t)(gbc >> 2);
+  }
+  // task i of the wave: slot (w0 + i) / G, row group gb0 + (w0 + i) % G
+  auto load_group = [&](int i, DownGroup<NI>& P) {
+    const bool live = i < n;
+    const int t = w0 + (live ? i : 0);
+    const int sl = __builtin_amdgcn_readfirstlane(t / G);
+    const uint32_t g = (uint32_t)(gb0 + (t - sl * G));
+    const bool sh = sl >= L.k;
+    const int e0 = sh ? 0 : ld_uniform(L.idx + sl);  // scalar load: no vector wait
+    const int e = e0 < 0 ? 0 : (e0 >= L.E ? L.E - 1 : e0);  // never address outside
+    const uint8_t* cb = (sh ? L.sd_codes : L.d_codes) + (size_t)e * mat_c;
+    const uint8_t* sb = (sh ? L.sd_scales : L.d_scales) + (size_t)e * mat_s;
+    const uint32_t soc = g * RPI * F2, sos = g * RPI * F32;
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const bool lv = live && ilive[u];
+      P.c[u] = buf_ld16(buf_rsrc(cb, lv ? mat_c : 0u), voc[u], soc);
+      P.sc[u] = buf_ld4(buf_rsrc(sb, lv ? mat_s : 0u), vos[u], sos);
+    }
+  };
+  DownGroup<NI> ring[D];
+#pragma unroll
+  for (int k = 0; k < D - 1; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_group(k, ring[k]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // activations in LDS (the compiler waits for the copies only)
+
+  // B operand of slot sl from LDS: 32 activation elements per block, column
+  // i4 (0: leading parts, 1: remainders, 2 and 3: zeros)
+  u32x4 bv[NI][4];
+  int bslot = -1;
+  auto load_b = [&](int sl) {
+    const uint16_t* ar = reinterpret_cast<const uint16_t*>(k3_smem) + (size_t)(i4 == 1 ? nslots + sl : sl) * L.F;
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int gb = t * CPR + cc;
+      const bool on = i4 < 2 && gb < nb;
+      const u32x4* src = reinterpret_cast<const u32x4*>(ar + 32 * (on ? gb : 0));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 v = src[u];
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        bv[t][u] = on ? v : z;
+      }
+    }
+  };
+  auto use_group = [&](int i, const DownGroup<NI>& P) {
+    const int t = w0 + i;
+    const int sl = __builtin_amdgcn_readfirstlane(t / G);
+    if (sl != bslot) {
+      load_b(sl);
+      bslot = sl;
+    }
+    const float ws = sl >= L.k ? 1.f : ld_uniform(L.wts + sl);
+    const f32x4 v = down_group_rows<CPR, NI>(P, bv, cc);
+    if ((lane & (GW - 1)) == GW - 1) {
+      const f32x4 o = {ws * v[0], ws * v[1], ws * v[2], ws * v[3]};
+      *reinterpret_cast<f32x4*>(&red[sl * srows + (t - sl * G) * RPI + 4 * rho]) = o;
+    }
+  };
+  bslot = __builtin_amdgcn_readfirstlane(w0 / G);
+  load_b(bslot);
+  int i = 0;
+  for (; i + D <= n; i += D) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      load_group(i + k + D - 1, ring[(k + D - 1) % D]);
+      __builtin_amdgcn_sched_barrier(0);
+      use_group(i + k, ring[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < D - 1; ++k)
+    if (i + k < n) use_group(i + k, ring[k]);
+  __syncthreads();
+
+  // slots summed in order, residual added
+  for (int r = (int)threadIdx.x; r < srows; r += (int)blockDim.x) {
+    float tot = 0.f;
+    for (int q = 0; q < nslots; ++q) tot += red[q * srows + r];
+    const int row = gb0 * RPI + r;
+    if (L.residual) tot += bf16_to_f32(L.residual[row]);
+    const uint16_t o = f32_to_bf16(tot);
+    L.out[row] = o;
+    if (L.trace) L.trace[row] = o;
   }
 }
 
@@ -954,12 +858,12 @@ hipError_t k2_launch(const LayerT1& L, const uint16_t* x, const int32_t* idx, fl
 
 // More than 64 KB of dynamic LDS needs the function's limit raised first
 // (set on every launch: cheap, and correct on whichever device is current).
-template <int LN>
-hipError_t k3_lds_launch(const LayerT1& L, int gpb, int nblk, size_t lds, hipStream_t s) {
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k3_down_lds<LN>),
+template <int CPR, int NI>
+hipError_t k3_slab_launch(const LayerT1& L, int gpb, int nblk, size_t lds, hipStream_t s) {
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k3_slab<CPR, NI>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k3_down_lds<LN>), dim3(nblk), dim3(kK3LdsWaves * kWave), lds, s, L, gpb);
+  hipLaunchKernelGGL((k3_slab<CPR, NI>), dim3(nblk), dim3(kK3SlabW * kWave), lds, s, L, gpb);
   return hipPeekAtLastError();
 }
 
@@ -1001,38 +905,46 @@ hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* 
 }
 
 hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s) {
-  const RowMap dm = down_map(L.F);
-  const int ngroups = L.H / (kWave / dm.lanes);
-  const int gpb = ceil_div(ngroups, kNumCU);  // one slab per CU
-  const int nblk = ceil_div(ngroups, gpb);
-  if (gpb * (kWave / dm.lanes) > kK3MaxRows) return hipErrorInvalidValue;
-  // one expert's down matrix is addressed through a 32-bit buffer descriptor
+  const int nslots = L.k + (L.S ? 1 : 0);
+  const int nb = L.F / 32;
+  if (L.F % 128 || L.H % 64 || nslots < 1) return hipErrorInvalidValue;
+  // one expert's down matrix is addressed through 32-bit buffer offsets
   if ((size_t)L.H * (size_t)(L.F / 2) > 0x7FFFFFFFu) return hipErrorInvalidValue;
-  const size_t act_bytes = (size_t)(L.k + (L.S ? 1 : 0)) * L.F * sizeof(float);
-  if (dm.bpl == 1 && act_bytes <= (size_t)kK3LdsActBytes) {
-    const size_t lds = act_bytes + (size_t)kK3LdsWaves * kK3MaxRows * sizeof(float);
-    switch (dm.lanes) {
-      case 64: return k3_lds_launch<64>(L, gpb, nblk, lds, s);
-      case 32: return k3_lds_launch<32>(L, gpb, nblk, lds, s);
-      case 16: return k3_lds_launch<16>(L, gpb, nblk, lds, s);
-      case 8: return k3_lds_launch<8>(L, gpb, nblk, lds, s);
-      case 4: return k3_lds_launch<4>(L, gpb, nblk, lds, s);
+  const int cpr = nb <= 4 ? 4 : (nb <= 8 ? 8 : 16);  // blocks per row per instruction
+  const int ninst = ceil_div(nb, cpr);               // instructions per row
+  const int ni = ninst >= 4 ? 4 : (ninst >= 2 ? 2 : 1);
+  const int kqn = ceil_div(ninst, ni);
+  {  // every slot in one workgroup when the activations fit in LDS
+    const int ni1 = ninst <= 1 ? 1 : (ninst <= 2 ? 2 : 4);
+    const int rpi = 64 / cpr, nrg = L.H / rpi;
+    const int gpb = ceil_div(nrg, kNumCU), nblk = ceil_div(nrg, gpb);
+    const size_t lds = 1024 * (size_t)ceil_div(4L * nslots * L.F, 1024) + 4 * (size_t)nslots * gpb * rpi;
+    if (ninst <= 4 && lds <= kK3SlabLds) {
+      if (cpr == 4) return k3_slab_launch<4, 1>(L, gpb, nblk, lds, s);
+      if (cpr == 8) return k3_slab_launch<8, 1>(L, gpb, nblk, lds, s);
+      if (ni1 == 1) return k3_slab_launch<16, 1>(L, gpb, nblk, lds, s);
+      if (ni1 == 2) return k3_slab_launch<16, 2>(L, gpb, nblk, lds, s);
+      return k3_slab_launch<16, 4>(L, gpb, nblk, lds, s);
     }
-    return hipErrorInvalidValue;
   }
-  const int per_wave = dm.bpl == 1 ? 2 : 1;  // routed slots streamed together
-  int nw = ceil_div(L.k, per_wave);
-  if (nw > kK3MaxWaves) nw = kK3MaxWaves;
-  if (nw * kWave < gpb * (kWave / dm.lanes)) nw = ceil_div(gpb * (kWave / dm.lanes), kWave);
-  const dim3 g(nblk), b(nw * kWave);
-#define K3(BP, LN) hipLaunchKernelGGL((k3_down_combine<BP, LN>), g, b, 0, s, L, dm.lanes, gpb)
-  if (dm.bpl == 2) K3(2, 64);
-  else if (dm.lanes == 64) K3(1, 64);
-  else if (dm.lanes == 32) K3(1, 32);
-  else if (dm.lanes == 16) K3(1, 16);
-  else if (dm.lanes == 8) K3(1, 8);
-  else if (dm.lanes == 4) K3(1, 4);
-  else return hipErrorInvalidValue;
+  const int maxw = kK3W;
+  if (kqn > maxw) return hipErrorInvalidValue;
+  const int nsn = maxw / kqn;
+  const int rpi = 64 / cpr, nrg = L.H / rpi;
+  // about one workgroup per CU, within the counters and the LDS slice sums
+  int nchunk = kNumCU / nslots;
+  if (nchunk < 1) nchunk = 1;
+  const int cap = nrg < kK3MaxChunks ? nrg : kK3MaxChunks;
+  if (nchunk > cap) nchunk = cap;
+  while (kqn * ceil_div(nrg, nchunk) * rpi > kK3RedFloats && nchunk < cap) ++nchunk;
+  if (kqn * ceil_div(nrg, nchunk) * rpi > kK3RedFloats) return hipErrorInvalidValue;
+  const dim3 g(nslots * nchunk), b(kqn * nsn * kWave);
+#define K3(C, N) hipLaunchKernelGGL((k3_down<C, N, k3_depth(N), kK3W>), g, b, 0, s, L, nchunk, kqn, nsn)
+  if (cpr == 4) K3(4, 1);
+  else if (cpr == 8) K3(8, 1);
+  else if (ni == 1) K3(16, 1);
+  else if (ni == 2) K3(16, 2);
+  else K3(16, 4);
 #undef K3
   return hipPeekAtLastError();
 }

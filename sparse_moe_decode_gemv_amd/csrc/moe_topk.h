@@ -14,15 +14,19 @@ namespace moe {
 //  1. Radix select, most significant byte first: four passes of a 256-bin
 //     LDS histogram over the keys that still match the chosen prefix, each
 //     followed by a wave scan from the top bin down, give the exact k-th
-//     largest key T and how many keys equal to T are needed (kr).
+//     largest key T and how many keys equal to T are needed (kr).  Each
+//     wave counts into a histogram of its own (logits share their leading
+//     bytes, so a shared histogram serialises most increments on a few
+//     bins); the scan adds the four.
 //  2. Keys above T, and the kr lowest-indexed keys equal to T, are gathered.
 //  3. One wave ranks the k gathered (key, index) pairs by (key desc, index
-//     asc) and writes them in that order with their softmax weights.
+//     asc), each lane holding one and reading the others from their lanes,
+//     and writes them in that order with their softmax weights.
 constexpr int kTopkBlock = 256;
 constexpr int kTopkPerThread = kMaxExperts / kTopkBlock;  // keys per thread
 
 struct TopkLds {
-  uint32_t hist[256];
+  uint32_t hist[kTopkBlock / kWave][256];  // one histogram per wave
   uint32_t sel_key[kMaxTopK];
   int32_t sel_idx[kMaxTopK];
   uint32_t wave_eq[kTopkBlock / kWave];
@@ -45,22 +49,26 @@ __device__ inline void topk_softmax_block(const float (&lg)[kTopkPerThread], int
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t decided = ~(0xFFFFFFFFu >> (8 * pass));  // bytes chosen so far
-    S.hist[tid] = 0u;
+#pragma unroll
+    for (int w = 0; w < kTopkBlock / kWave; ++w) S.hist[w][tid] = 0u;
     if (tid == 0) S.nsel = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const bool match = ((key[i] ^ prefix) & decided) == 0u;
-      if (match && key[i] != 0u) atomicAdd(&S.hist[(key[i] >> shift) & 255u], 1u);
+      if (match && key[i] != 0u) atomicAdd(&S.hist[wid][(key[i] >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (wid == 0) {
-      // lane l holds bins 255-4l .. 252-4l (descending)
+      // lane l holds bins 255-4l .. 252-4l (descending), summed over waves
       uint32_t cnt[4], tot = 0u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        cnt[j] = S.hist[255 - 4 * lane - j];
-        tot += cnt[j];
+        uint32_t c = 0u;
+#pragma unroll
+        for (int w = 0; w < kTopkBlock / kWave; ++w) c += S.hist[w][255 - 4 * lane - j];
+        cnt[j] = c;
+        tot += c;
       }
       const uint32_t incl = wave_incl_scan_u32(tot);
       const uint64_t over = __ballot(incl >= (uint32_t)kr);
@@ -116,11 +124,15 @@ __device__ inline void topk_softmax_block(const float (&lg)[kTopkPerThread], int
     const bool act = lane < k;
     const uint32_t mk = act ? S.sel_key[lane] : 0u;
     const int mi = act ? S.sel_idx[lane] : 0;
+    // rank against every candidate, read from its lane (no LDS round trips)
     int rank = 0;
-    for (int j = 0; j < k; ++j) {
-      const uint32_t kj = S.sel_key[j];
-      const int ij = S.sel_idx[j];
-      rank += (kj > mk || (kj == mk && ij < mi)) ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
+        const int ij = __builtin_amdgcn_readlane(mi, j);
+        rank += (kj > mk || (kj == mk && ij < mi)) ? 1 : 0;
+      }
     }
     const uint32_t top = wave_max_u32(mk);
     const float l = f32_from_order_key(mk);

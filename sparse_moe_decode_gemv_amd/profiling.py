@@ -28,7 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(HERE, "csrc", "moe_t1.hip")
 CALIB_BYTES = 1 << 30
 
-_NAMES = re.compile(r"(k1_router|k1_topk|k2_gateup|k3_down_lds|k3_down_combine|kb_\w+|"
+_NAMES = re.compile(r"(k1_router|k1_topk|k2_gateup|k3_slab|k3_down|kb_\w+|"
                     r"zero_fill_kernel|fill_\w+_kernel|copyBuffer\w*|\w+_kernel)")
 
 

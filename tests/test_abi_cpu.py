@@ -40,7 +40,7 @@ def test_workspace_size_grows_with_tokens():
     ((16384, 896, 16, 2048, 1, 2048), M.MOE_ERR_UNSUPPORTED),  # H too large
     ((2304, 64, 4, 256, 0, 0), M.MOE_ERR_UNSUPPORTED),         # 9 blocks per lane
     ((7168, 896, 16, 2000, 1, 2000), M.MOE_ERR_UNSUPPORTED),   # F % 128
-    ((7168, 896, 16, 384, 1, 384), M.MOE_ERR_UNSUPPORTED),     # 3 blocks per lane
+    ((7168, 896, 16, 8320, 1, 8320), M.MOE_ERR_UNSUPPORTED),   # F > 8192
     ((7168, 896, 16, 2048, 1, 1024), M.MOE_ERR_UNSUPPORTED),   # Fs != F
     ((7168, 896, 16, 2048, 2, 2048), M.MOE_ERR_UNSUPPORTED),   # two shared
     ((7168, 2048, 16, 2048, 0, 0), M.MOE_ERR_UNSUPPORTED),     # E > 1024

@@ -22,6 +22,11 @@ SMALL = {
     "one_expert": G.Workload("one_expert", T=1, H=256, E=1, k=1, F=128, S=1, Fs=128, seed=0x5EED0104),
     "wide_f": G.Workload("wide_f", T=1, H=2048, E=24, k=4, F=4096, S=1, Fs=4096, seed=0x5EED0105),
     "h8192": G.Workload("h8192", T=1, H=8192, E=20, k=3, F=1024, S=0, Fs=0, seed=0x5EED0106),
+    # F/32 not a multiple of the 16 blocks one down load instruction covers
+    "f384": G.Workload("f384", T=1, H=512, E=12, k=3, F=384, S=1, Fs=384, seed=0x5EED0108),
+    "f640": G.Workload("f640", T=1, H=768, E=10, k=2, F=640, S=0, Fs=0, seed=0x5EED0109),
+    "f1536": G.Workload("f1536", T=1, H=1024, E=8, k=2, F=1536, S=1, Fs=1536, seed=0x5EED010A),
+    "f8192": G.Workload("f8192", T=1, H=256, E=4, k=2, F=8192, S=1, Fs=8192, seed=0x5EED010B),
 }
 
 
