@@ -2,7 +2,7 @@
 //
 //  K1a router GEMV over all E rows (one wave per row, every load of the row
 //      in flight at once).
-//  K2  top-k + softmax (radix select) in every workgroup, then gate/up GEMVs
+//  K2  top-k + softmax (one wave per workgroup) in every workgroup, then gate/up GEMVs
 //      with fused MXFP4 dequant and SiLU gating -> gated activations (fp32
 //      for the gate/up entry point; in the layer, two bf16 parts for K3):
 //      first the shared expert's rows, then those of the k selected experts.  The
@@ -389,16 +389,48 @@ __global__ __launch_bounds__(kBlock) void k1_router(LayerT1 L) {
   }
 }
 
-// K1b (router-only entry point): top-k + softmax of the logits, one workgroup.
-__global__ __launch_bounds__(kBlock) void k1_topk(LayerT1 L) {
-  __shared__ TopkLds tk;
+// Lane l of a wave: router logits 16 l .. 16 l + 15 (four 16-byte loads),
+// then as order-preserving keys (experts past E are absent: key 0).
+__device__ __forceinline__ void load_logits16(const float* logits, int E, f32x4 (&v)[4]) {
+  const int lane = threadIdx.x & 63;
+  const auto rl = buf_rsrc(logits, 4u * (uint32_t)E);  // E = 0: zeros, no access
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, 64 * lane + 16 * q, 0, 0));
+}
+__device__ __forceinline__ void logit_keys16(const f32x4 (&v)[4], int E, uint32_t (&key)[16]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) key[4 * q + c] = 16 * lane + 4 * q + c < E ? f32_order_key(v[q][c]) : 0u;
+}
+
+// The block selection, for the rare logit sets the wave selection declines.
+__device__ __forceinline__ void topk_block_fallback(const LayerT1& L, TopkLds& tk, int32_t* idx, float* wts,
+                                                    int32_t* idx_out, float* w_out) {
   float lg[kTopkPerThread];
 #pragma unroll
   for (int i = 0; i < kTopkPerThread; ++i) {
     const int e = threadIdx.x * kTopkPerThread + i;
     lg[i] = L.logits[e < L.E ? e : L.E - 1];
   }
-  topk_softmax_block(lg, L.E, L.k, tk, L.idx, L.wts, L.idx_out, L.w_out);
+  topk_softmax_block(lg, L.E, L.k, tk, idx, wts, idx_out, w_out);
+}
+
+// K1b (router-only entry point): top-k + softmax of the logits, one workgroup.
+__global__ __launch_bounds__(kBlock) void k1_topk(LayerT1 L) {
+  __shared__ TopkLds tk;
+  if (wave_id() == 0) {
+    f32x4 lv[4];
+    uint32_t key[16];
+    load_logits16(L.logits, L.E, lv);
+    logit_keys16(lv, L.E, key);
+    const bool ok = topk_softmax_wave(key, L.E, L.k, tk, L.idx, L.wts, L.idx_out, L.w_out);
+    if ((threadIdx.x & 63) == 0) tk.wave_ok = ok ? 1 : 0;
+  }
+  __syncthreads();
+  if (!tk.wave_ok) topk_block_fallback(L, tk, L.idx, L.wts, L.idx_out, L.w_out);
 }
 
 // Two waves per SIMD for the gate/up kernel: three (at most 168 registers)
@@ -430,31 +462,36 @@ __global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, 
   const int first = blockIdx.x * kWaves + wid, ntask = ns + L.k * g.tps;
   // Request order matters: loads complete in order for the wait counter, so
   // the selection's inputs go first and the shared weights last; waiting
-  // for the logits then leaves the shared weights in flight.
-  float lg[kTopkPerThread];
-  int32_t e_in = 0;
-  if (idx) {
-    e_in = idx[threadIdx.x < L.k ? threadIdx.x : 0];
-  } else {
-#pragma unroll
-    for (int i = 0; i < kTopkPerThread; ++i) {
-      const int e = threadIdx.x * kTopkPerThread + i;
-      lg[i] = L.logits[e < L.E ? e : L.E - 1];
-    }
-  }
+  // for the logits then leaves the shared weights in flight.  Wave 0 makes
+  // the selection alone (no barrier inside it).
+  // (both requested unconditionally, one of them through an empty
+  // descriptor, so that every path has the same loads in flight)
+  f32x4 lv[4];
+  const int32_t e_in = (int32_t)buf_ld4(buf_rsrc(idx, idx ? 4u * (uint32_t)L.k : 0u),
+                                        4u * (threadIdx.x < L.k ? threadIdx.x : 0u), 0u);
+  load_logits16(L.logits, idx ? 0 : L.E, lv);
   XStage xs;
   stage_x_load(x, L.H, xs);
   uint4 ca[BPLH];
   uint32_t sa[BPLH];
-  const bool early = PRE && first < ns;  // wave-uniform
+  constexpr bool early = PRE;  // the launcher gives every wave a shared first task
   if (early) g.load(J, first, ca, sa);
   if (idx) {
     if (threadIdx.x < L.k)
       e_lds[threadIdx.x] = e_in < 0 ? 0 : (e_in >= L.E ? L.E - 1 : e_in);  // never address outside
     __syncthreads();
   } else {
-    topk_softmax_block(lg, L.E, L.k, tk, e_lds, w_lds, nullptr, nullptr);
+    if (wid == 0) {
+      uint32_t key[16];
+      logit_keys16(lv, L.E, key);
+      const bool ok = topk_softmax_wave(key, L.E, L.k, tk, e_lds, w_lds, nullptr, nullptr);
+      if ((threadIdx.x & 63) == 0) tk.wave_ok = ok ? 1 : 0;
+    }
     __syncthreads();
+    if (!tk.wave_ok) {  // many equal logits at the threshold
+      topk_block_fallback(L, tk, e_lds, w_lds, nullptr, nullptr);
+      __syncthreads();
+    }
   }
   if (!early) g.load(J, first < ntask ? first : ntask - 1, ca, sa);
   stage_x_store(xs, L.H, x_lds);

@@ -26,6 +26,9 @@ constexpr int kTopkBlock = 256;
 constexpr int kTopkPerThread = kMaxExperts / kTopkBlock;  // keys per thread
 
 struct TopkLds {
+  uint32_t cand_key[kWave];  // wave top-k: compacted candidates
+  int32_t cand_idx[kWave];
+  int32_t wave_ok;           // wave top-k done (else the block fallback runs)
   uint32_t hist[kTopkBlock / kWave][256];  // one histogram per wave
   uint32_t sel_key[kMaxTopK];
   int32_t sel_idx[kMaxTopK];
@@ -146,6 +149,75 @@ __device__ inline void topk_softmax_block(const float (&lg)[kTopkPerThread], int
       if (w_out) w_out[rank] = w;
     }
   }
+}
+
+// Top-k + softmax by ONE wave, without barriers (E <= 1024, k <= 32).  Lane l
+// holds experts 16 l .. 16 l + 15 as order-preserving keys (key[m], 0 for an
+// absent expert); the order is the block version's: larger logit first,
+// lower index first among equal logits.
+//  1. T = the k-th largest of the 64 lane maxima (lanes ranked by (key,
+//     lane)): at least k keys are >= T, so every selected key is.
+//  2. The present keys >= T (C of them, C >= k; about k + 2 for random
+//     logits) are compacted in expert order into S.cand_* by a wave scan.
+//  3. Candidate j (lane j) is ranked against the others by (key desc, index
+//     asc); ranks below k are the selection, written in that order with
+//     their softmax weights.
+// Returns false, writing nothing, when C > 64 (only with many equal logits
+// at the threshold); the caller then runs topk_softmax_block.
+__device__ inline bool topk_softmax_wave(const uint32_t (&key)[16], int E, int k, TopkLds& S,
+                                         int32_t* idx, float* wts, int32_t* idx_out, float* w_out) {
+  const int lane = threadIdx.x & 63;
+  // 1. lane maximum (the first of equal keys: the lower index) and its rank
+  uint32_t lm = 0u;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) lm = key[m] > lm ? key[m] : lm;
+  int rank = 0;
+  for (int j = 0; j < kWave; ++j) {
+    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)lm, j);
+    rank += (kj > lm || (kj == lm && j < lane)) ? 1 : 0;
+  }
+  const uint64_t at = __ballot(rank == k - 1);
+  const uint32_t T = (uint32_t)__builtin_amdgcn_readlane((int)lm, (int)__builtin_ctzll(at));
+  // 2. present keys >= T, compacted in expert order
+  const int base = lane * 16;
+  uint32_t cnt = 0u;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) cnt += (base + m < E && key[m] >= T) ? 1u : 0u;
+  const uint32_t incl = wave_incl_scan_u32(cnt);
+  const int C = __builtin_amdgcn_readlane((int)incl, kWave - 1);
+  if (C > kWave) return false;
+  uint32_t pos = incl - cnt;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    if (base + m < E && key[m] >= T) {
+      S.cand_key[pos] = key[m];
+      S.cand_idx[pos] = base + m;
+      ++pos;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  const bool act = lane < C;
+  const uint32_t ck = act ? S.cand_key[lane] : 0u;
+  const int ci = act ? S.cand_idx[lane] : 0;
+  // 3. exact rank among the candidates
+  int r = 0;
+  for (int j = 0; j < C; ++j) {
+    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ck, j);
+    const int ij = __builtin_amdgcn_readlane(ci, j);
+    r += (kj > ck || (kj == ck && ij < ci)) ? 1 : 0;
+  }
+  const bool sel = act && r < k;
+  const uint32_t top = wave_max_u32(sel ? ck : 0u);
+  const float ex = sel ? expf(f32_from_order_key(ck) - f32_from_order_key(top)) : 0.f;
+  const float sum = wave_sum(ex);
+  if (sel) {
+    const float w = ex / sum;
+    idx[r] = ci;
+    wts[r] = w;
+    if (idx_out) idx_out[r] = ci;
+    if (w_out) w_out[r] = w;
+  }
+  return true;
 }
 
 }  // namespace moe

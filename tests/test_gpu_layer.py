@@ -149,6 +149,64 @@ def test_zero_activation_ties_pick_lowest_experts():
     np.testing.assert_array_equal(out, r)
 
 
+def _router_entry(w, dl, x):
+    t = torch()
+    idx = t.empty((1, w.k), dtype=t.int32, device="cuda")
+    wts = t.empty((1, w.k), dtype=t.float32, device="cuda")
+    ws = workspace(w, 1)
+    M.router_topk(shape_of(w), dev_u16(x.reshape(1, -1)), dl.router, 1, idx, wts, None, ws)
+    t.cuda.synchronize()
+    return idx.cpu().numpy(), wts.cpu().numpy()
+
+
+def test_all_logits_equal_with_many_experts():
+    """x = 0 with E = 896: all 896 logits tie, far more than one wave's
+    candidate list holds, so the block selection runs; it must still pick
+    experts 0..k-1 with weight 1/k, in both entry points."""
+    w = G.WORKLOADS["k3_batch1"]
+    dl = device_layer(w, 0)
+    x = np.zeros(w.H, np.uint16)
+    out, idx, wts = run_layer(w, dl, x)
+    assert idx[0].tolist() == list(range(w.k))
+    np.testing.assert_array_equal(wts[0], np.full(w.k, 1.0 / w.k, np.float32))
+    ridx, rwts = _router_entry(w, dl, x)
+    assert ridx[0].tolist() == list(range(w.k))
+    np.testing.assert_array_equal(rwts[0], np.full(w.k, 1.0 / w.k, np.float32))
+
+
+@pytest.mark.parametrize("copies", [20, 70])
+def test_duplicated_top_router_row(copies):
+    """The router row of the token's best expert is copied into `copies`
+    other rows, so that many logits tie exactly at the top: the selection is
+    the lowest-indexed k of them (20 copies: the one-wave selection; 70: more
+    ties than it holds, the block selection).  Checked against the oracle's
+    exact selection in both entry points."""
+    w = G.WORKLOADS["k3_batch1"]
+    dl = device_layer(w, 0)
+    try:
+        x = G.token(w, 11)
+        R = dl.router_host.copy()
+        L0 = O.router_logits(x, R)
+        best = int(np.argmax(L0))
+        rng = np.random.default_rng(copies)
+        others = rng.choice([e for e in range(w.E) if e != best], copies, replace=False)
+        R[others] = R[best]
+        dl.router.copy_(dev_u16(R))
+        dl.router_host = R
+        L = O.router_logits(x, R)
+        ref = O.topk_select(L, w.k)
+        ref_w = O.topk_weights(L, ref)[0]
+        ref = [int(e) for e in ref[0]]
+        out, idx, wts = run_layer(w, dl, x)
+        assert idx[0].tolist() == ref, (idx[0].tolist(), ref)
+        np.testing.assert_allclose(wts[0], ref_w, atol=2e-6)
+        ridx, rwts = _router_entry(w, dl, x)
+        assert ridx[0].tolist() == ref
+        np.testing.assert_allclose(rwts[0], ref_w, atol=2e-6)
+    finally:
+        device_layer.cache_clear()
+
+
 def test_no_residual_and_in_place_output():
     t = torch()
     w = G.WORKLOADS["tiny"]
