@@ -118,7 +118,9 @@ int moe_router_topk(const moe_shape* shape, const uint16_t* x, const uint16_t* r
 /* Gate/up projections of the selected experts with SiLU gating:
  *   act[t][j][f] = silu(G_e x_t)[f] * (U_e x_t)[f],  e = topk_idx[t][j]
  * computed in fp32 from the MXFP4 weights (dequantised in the dot product).
- * topk_idx int32 [T][k] (device), act fp32 [T][k][F] out.
+ * topk_idx int32 [T][k] (device; clamped to [0, E) before addressing),
+ * act fp32 [T][k][F] out.  T must be 0 or 1 (T > 1: MOE_ERR_UNSUPPORTED;
+ * the batched layer runs its own grouped gate/up).
  * This is the layer's dominant HBM stream, exported for measurement. */
 int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
                       const int32_t* topk_idx, int32_t n_tokens, float* act,
@@ -127,7 +129,9 @@ int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const 
 /* One MoE decode layer:
  *   out[t] = residual[t] + sum_j topk_w[t][j] * y_{idx[t][j]}(x_t) + y_shared(x_t)
  *   y_e(x) = D_e (silu(G_e x) * (U_e x)), shared expert weight 1
- * rounded once to bf16 (nearest even).
+ * rounded once to bf16 (nearest even).  T = 1 runs the single-token kernels;
+ * 2 <= T <= 64 groups the (token, slot) pairs by expert and runs grouped
+ * MFMA kernels (each selected expert's weights are read once per call).
  * x        bf16 [T][H]
  * residual bf16 [T][H] or NULL (no residual); may equal x
  * out      bf16 [T][H]; may equal residual, must not overlap x otherwise
@@ -151,8 +155,11 @@ int moe_decode_stack(const moe_shape* shape, const moe_layer_weights* layers,
 
 /* Token grouping used by the batched path: a stable counting sort of the
  * T*k (token, slot) pairs by expert.
+ *   topk_idx int32 [T][k] (device); values are clamped to [0, E)
  *   offsets int32 [E+1] out: pairs of expert e are pairs[offsets[e]..offsets[e+1])
- *   pairs   int32 [T*k] out: t*k + j, increasing within each expert */
+ *   pairs   int32 [T*k] out: t*k + j, increasing within each expert
+ * 0 <= T <= 64, 1 <= k <= min(E, 32), E <= 1024; ws as from
+ * moe_workspace_size for any shape with these E, k and at least T tokens. */
 int moe_group_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t top_k,
                         int32_t n_experts, int32_t* offsets, int32_t* pairs,
                         void* ws, size_t ws_bytes, void* stream);
