@@ -323,19 +323,26 @@ struct GateUp {
     if (LANES) acc = group_sum_last_c<LANES ? LANES : 32>(acc);
     else acc = group_sum_last(acc, lanes);
     const float up = __shfl_xor(acc, 32, kWave);
-    if (half == 0 && col == lanes - 1) {
-      bool sh;
-      int slot, j;
-      locate(J, t, sh, slot, j);
-      const float a = silu(acc) * up;
-      if (J.act_hl) {  // a = hi + lo to about 16 significant bits
-        const uint16_t hi = f32_to_bf16(a);
-        const float d = a - bf16_to_f32(hi);
-        J.act_hl[(size_t)slot * J.F + j] = hi;
-        J.act_hl[(size_t)(J.nslot + slot) * J.F + j] = f32_to_bf16(d == d ? d : 0.f);
-      } else {
-        J.act[(size_t)slot * J.F + j] = a;
-      }
+    // Every lane stores; only a row's owner (the last lane of its gate group)
+    // has an offset inside the buffer, the others' stores are dropped by the
+    // range check.  No branch, so the wait counts of the task loop stay exact.
+    bool sh;
+    int slot, j;
+    locate(J, t, sh, slot, j);
+    const bool own = half == 0 && col == lanes - 1;
+    const float a = silu(acc) * up;
+    if (J.act_hl) {  // a = hi + lo to about 16 significant bits
+      const uint16_t hi = f32_to_bf16(a);
+      const float d = a - bf16_to_f32(hi);
+      const uint16_t lo = f32_to_bf16(d == d ? d : 0.f);
+      const auto r = buf_rsrc(J.act_hl, 4u * (uint32_t)J.nslot * (uint32_t)J.F);
+      const uint32_t o = own ? 2u * (uint32_t)(slot * J.F + j) : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_buffer_store_b16(hi, r, (int)o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(lo, r, (int)(own ? o + 2u * (uint32_t)(J.nslot * J.F) : o), 0, 0);
+    } else {
+      const auto r = buf_rsrc(J.act, 4u * (uint32_t)(J.k + 1) * (uint32_t)J.F);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r,
+                                            (int)(own ? 4u * (uint32_t)(slot * J.F + j) : 0xFFFFFFF0u), 0, 0);
     }
   }
 };
@@ -406,18 +413,6 @@ __device__ __forceinline__ void logit_keys16(const f32x4 (&v)[4], int E, uint32_
     for (int c = 0; c < 4; ++c) key[4 * q + c] = 16 * lane + 4 * q + c < E ? f32_order_key(v[q][c]) : 0u;
 }
 
-// The block selection, for the rare logit sets the wave selection declines.
-__device__ __forceinline__ void topk_block_fallback(const LayerT1& L, TopkLds& tk, int32_t* idx, float* wts,
-                                                    int32_t* idx_out, float* w_out) {
-  float lg[kTopkPerThread];
-#pragma unroll
-  for (int i = 0; i < kTopkPerThread; ++i) {
-    const int e = threadIdx.x * kTopkPerThread + i;
-    lg[i] = L.logits[e < L.E ? e : L.E - 1];
-  }
-  topk_softmax_block(lg, L.E, L.k, tk, idx, wts, idx_out, w_out);
-}
-
 // K1b (router-only entry point): top-k + softmax of the logits, one workgroup.
 __global__ __launch_bounds__(kBlock) void k1_topk(LayerT1 L) {
   __shared__ TopkLds tk;
@@ -426,11 +421,9 @@ __global__ __launch_bounds__(kBlock) void k1_topk(LayerT1 L) {
     uint32_t key[16];
     load_logits16(L.logits, L.E, lv);
     logit_keys16(lv, L.E, key);
-    const bool ok = topk_softmax_wave(key, L.E, L.k, tk, L.idx, L.wts, L.idx_out, L.w_out);
-    if ((threadIdx.x & 63) == 0) tk.wave_ok = ok ? 1 : 0;
+    if (!topk_softmax_wave(key, L.E, L.k, tk, L.idx, L.wts, L.idx_out, L.w_out))
+      topk_softmax_wave_rounds(key, L.E, L.k, L.idx, L.wts, L.idx_out, L.w_out);  // many ties
   }
-  __syncthreads();
-  if (!tk.wave_ok) topk_block_fallback(L, tk, L.idx, L.wts, L.idx_out, L.w_out);
 }
 
 // Two waves per SIMD for the gate/up kernel: three (at most 168 registers)
@@ -484,14 +477,10 @@ __global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, 
     if (wid == 0) {
       uint32_t key[16];
       logit_keys16(lv, L.E, key);
-      const bool ok = topk_softmax_wave(key, L.E, L.k, tk, e_lds, w_lds, nullptr, nullptr);
-      if ((threadIdx.x & 63) == 0) tk.wave_ok = ok ? 1 : 0;
+      if (!topk_softmax_wave(key, L.E, L.k, tk, e_lds, w_lds, nullptr, nullptr))
+        topk_softmax_wave_rounds(key, L.E, L.k, e_lds, w_lds, nullptr, nullptr);  // many ties
     }
     __syncthreads();
-    if (!tk.wave_ok) {  // many equal logits at the threshold
-      topk_block_fallback(L, tk, e_lds, w_lds, nullptr, nullptr);
-      __syncthreads();
-    }
   }
   if (!early) g.load(J, first < ntask ? first : ntask - 1, ca, sa);
   stage_x_store(xs, L.H, x_lds);

@@ -28,7 +28,6 @@ constexpr int kTopkPerThread = kMaxExperts / kTopkBlock;  // keys per thread
 struct TopkLds {
   uint32_t cand_key[kWave];  // wave top-k: compacted candidates
   int32_t cand_idx[kWave];
-  int32_t wave_ok;           // wave top-k done (else the block fallback runs)
   uint32_t hist[kTopkBlock / kWave][256];  // one histogram per wave
   uint32_t sel_key[kMaxTopK];
   int32_t sel_idx[kMaxTopK];
@@ -163,7 +162,7 @@ __device__ inline void topk_softmax_block(const float (&lg)[kTopkPerThread], int
 //     asc); ranks below k are the selection, written in that order with
 //     their softmax weights.
 // Returns false, writing nothing, when C > 64 (only with many equal logits
-// at the threshold); the caller then runs topk_softmax_block.
+// at the threshold); the caller then runs topk_softmax_wave_rounds.
 __device__ inline bool topk_softmax_wave(const uint32_t (&key)[16], int E, int k, TopkLds& S,
                                          int32_t* idx, float* wts, int32_t* idx_out, float* w_out) {
   const int lane = threadIdx.x & 63;
@@ -218,6 +217,55 @@ __device__ inline bool topk_softmax_wave(const uint32_t (&key)[16], int E, int k
     if (w_out) w_out[r] = w;
   }
   return true;
+}
+
+// The same selection by k rounds of a wave argmax over (key, lower index):
+// exact for any logits (ties included), slower (about 70 instructions a
+// round); the fallback when topk_softmax_wave declines.
+__device__ inline void topk_softmax_wave_rounds(uint32_t (&key)[16], int E, int k, int32_t* idx,
+                                                float* wts, int32_t* idx_out, float* w_out) {
+  const int lane = threadIdx.x & 63;
+  const int base = lane * 16;
+#pragma unroll
+  for (int m = 0; m < 16; ++m)
+    if (base + m >= E) key[m] = 0u;
+  uint32_t sk = 0u;  // this lane's pick of round r (lane r keeps round r's)
+  int si = 0;
+  for (int r = 0; r < k; ++r) {
+    // lane best: the largest key, the lowest index among equals
+    uint32_t bk = 0u;
+    int bm = 0;
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      if (key[m] > bk) {
+        bk = key[m];
+        bm = m;
+      }
+    const uint32_t K = wave_max_u32(bk);
+    const uint64_t has = __ballot(bk == K);
+    const int wl = (int)__builtin_ctzll(has);  // lowest lane: lowest index
+    const int wm = __builtin_amdgcn_readlane(bm, wl);
+    if (lane == r) {
+      sk = K;
+      si = wl * 16 + wm;
+    }
+    if (lane == wl) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+        if (m == wm) key[m] = 0u;
+    }
+  }
+  const bool sel = lane < k;
+  const uint32_t top = (uint32_t)__builtin_amdgcn_readlane((int)sk, 0);
+  const float ex = sel ? expf(f32_from_order_key(sk) - f32_from_order_key(top)) : 0.f;
+  const float sum = wave_sum(ex);
+  if (sel) {
+    const float w = ex / sum;
+    idx[lane] = si;
+    wts[lane] = w;
+    if (idx_out) idx_out[lane] = si;
+    if (w_out) w_out[lane] = w;
+  }
 }
 
 }  // namespace moe
