@@ -279,8 +279,24 @@ struct GateUp {
     const size_t row = (size_t)(sh ? 0 : e) * J.F + j;
     const uint8_t* cb = (sh ? shc : rc) + row * (size_t)(J.H / 2);
     const uint8_t* sb = (sh ? shs : rs) + row * (size_t)(J.H / 32);
-    if (LANES) {
-      // lane base once, constant strides: immediate offsets on the loads
+    if (LANES == 32) {
+      // lane base once, constant strides: immediate offsets on the loads.
+      // The row's 8 BPL scale dwords come in one or two loads (lane col:
+      // dwords col and col + 32, clamped to the row); finish() fetches each
+      // block's dword from its lane with ds_bpermute.
+      const u32x4* cp = reinterpret_cast<const u32x4*>(cb) + col;
+      const uint32_t* sw = reinterpret_cast<const uint32_t*>(sb);
+      constexpr int ND = 8 * BPL;  // scale dwords of a row
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        const u32x4 t = __builtin_nontemporal_load(cp + LANES * i);
+        c[i] = make_uint4(t.x, t.y, t.z, t.w);
+      }
+      sc[0] = __builtin_nontemporal_load(sw + (col < ND ? col : ND - 1));
+      if (BPL > 4) sc[1] = __builtin_nontemporal_load(sw + (col + 32 < ND ? col + 32 : ND - 1));
+#pragma unroll
+      for (int i = (BPL > 4 ? 2 : 1); i < BPL; ++i) sc[i] = 0u;
+    } else if (LANES) {
       const u32x4* cp = reinterpret_cast<const u32x4*>(cb) + col;
       const uint32_t* sp = reinterpret_cast<const uint32_t*>(sb) + (col >> 2);
 #pragma unroll
@@ -299,7 +315,18 @@ struct GateUp {
     }
   }
   __device__ __forceinline__ void finish(const GateUpJob& J, const uint32_t* x_lds, int t,
-                                         const uint4 (&c)[BPL], const uint32_t (&sc)[BPL]) const {
+                                         const uint4 (&c)[BPL], const uint32_t (&sc_in)[BPL]) const {
+    uint32_t sc[BPL];
+    if (LANES == 32) {  // block col + 32 i's dword (col / 4 + 8 i) from the lane holding it
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i)
+        sc[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((lane & 32) + (((col >> 2) + 8 * i) & 31)),
+                                                       (int)sc_in[i < 4 ? 0 : 1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) sc[i] = sc_in[i];
+    }
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
@@ -734,7 +761,11 @@ constexpr int kK3SlabW = 8;                  // waves per workgroup (two per SIM
 constexpr int kK3SlabD = 4;                  // row groups in flight per wave
 constexpr size_t kK3SlabLds = 156 * 1024;    // LDS budget: activations + row sums
 
-template <int CPR, int NI>
+// SC1 (F = 512 NI exactly, 16 blocks per instruction): one scale dword per
+// lane and group, lane 4b+i holding dword b of row i's scales; the dword
+// with block 16t + b's byte is then fetched from lane 4(4t + b/4) + i by
+// ds_bpermute, one vector-memory instruction per group instead of NI.
+template <int CPR, int NI, bool SC1>
 __global__ __launch_bounds__(kK3SlabW * kWave) void k3_slab(LayerT1 L, int gpb) {
   constexpr int RPI = 64 / CPR, GW = 4 * CPR, D = kK3SlabD, W = kK3SlabW;
   extern __shared__ __align__(16) uint8_t k3_smem[];
@@ -771,6 +802,7 @@ __global__ __launch_bounds__(kK3SlabW * kWave) void k3_slab(LayerT1 L, int gpb) 
     voc[t] = row_in * F2 + 16u * (uint32_t)gbc;
     vos[t] = row_in * F32 + 4u * (uint32_t)(gbc >> 2);
   }
+  const uint32_t vos1 = row_in * F32 + 4u * (uint32_t)b;  // SC1: dword b of the row
   // task i of the wave: slot (w0 + i) / G, row group gb0 + (w0 + i) % G
   auto load_group = [&](int i, DownGroup<NI>& P) {
     const bool live = i < n;
@@ -787,8 +819,10 @@ __global__ __launch_bounds__(kK3SlabW * kWave) void k3_slab(LayerT1 L, int gpb) 
     for (int u = 0; u < NI; ++u) {
       const bool lv = live && ilive[u];
       P.c[u] = buf_ld16(buf_rsrc(cb, lv ? mat_c : 0u), voc[u], soc);
-      P.sc[u] = buf_ld4(buf_rsrc(sb, lv ? mat_s : 0u), vos[u], sos);
+      if (!SC1) P.sc[u] = buf_ld4(buf_rsrc(sb, lv ? mat_s : 0u), vos[u], sos);
+      else if (u > 0) P.sc[u] = 0u;
     }
+    if (SC1) P.sc[0] = buf_ld4(buf_rsrc(sb, live ? mat_s : 0u), vos1, sos);
   };
   DownGroup<NI> ring[D];
 #pragma unroll
@@ -826,7 +860,16 @@ __global__ __launch_bounds__(kK3SlabW * kWave) void k3_slab(LayerT1 L, int gpb) 
       bslot = sl;
     }
     const float ws = sl >= L.k ? 1.f : ld_uniform(L.wts + sl);
-    const f32x4 v = down_group_rows<CPR, NI>(P, bv, cc);
+    f32x4 v;
+    if (SC1) {
+      DownGroup<NI> Q = P;
+#pragma unroll
+      for (int t = 0; t < NI; ++t)
+        Q.sc[t] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (16 * t + 4 * (b >> 2) + i4), (int)P.sc[0]);
+      v = down_group_rows<CPR, NI>(Q, bv, cc);
+    } else {
+      v = down_group_rows<CPR, NI>(P, bv, cc);
+    }
     if ((lane & (GW - 1)) == GW - 1) {
       const f32x4 o = {ws * v[0], ws * v[1], ws * v[2], ws * v[3]};
       *reinterpret_cast<f32x4*>(&red[sl * srows + (t - sl * G) * RPI + 4 * rho]) = o;
@@ -884,12 +927,12 @@ hipError_t k2_launch(const LayerT1& L, const uint16_t* x, const int32_t* idx, fl
 
 // More than 64 KB of dynamic LDS needs the function's limit raised first
 // (set on every launch: cheap, and correct on whichever device is current).
-template <int CPR, int NI>
+template <int CPR, int NI, bool SC1 = false>
 hipError_t k3_slab_launch(const LayerT1& L, int gpb, int nblk, size_t lds, hipStream_t s) {
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k3_slab<CPR, NI>),
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k3_slab<CPR, NI, SC1>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k3_slab<CPR, NI>), dim3(nblk), dim3(kK3SlabW * kWave), lds, s, L, gpb);
+  hipLaunchKernelGGL((k3_slab<CPR, NI, SC1>), dim3(nblk), dim3(kK3SlabW * kWave), lds, s, L, gpb);
   return hipPeekAtLastError();
 }
 
@@ -949,8 +992,11 @@ hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s) {
       if (cpr == 4) return k3_slab_launch<4, 1>(L, gpb, nblk, lds, s);
       if (cpr == 8) return k3_slab_launch<8, 1>(L, gpb, nblk, lds, s);
       if (ni1 == 1) return k3_slab_launch<16, 1>(L, gpb, nblk, lds, s);
-      if (ni1 == 2) return k3_slab_launch<16, 2>(L, gpb, nblk, lds, s);
-      return k3_slab_launch<16, 4>(L, gpb, nblk, lds, s);
+      if (ni1 == 2)
+        return nb == 32 ? k3_slab_launch<16, 2, true>(L, gpb, nblk, lds, s)
+                        : k3_slab_launch<16, 2>(L, gpb, nblk, lds, s);
+      return nb == 64 ? k3_slab_launch<16, 4, true>(L, gpb, nblk, lds, s)
+                      : k3_slab_launch<16, 4>(L, gpb, nblk, lds, s);
     }
   }
   const int maxw = kK3W;
