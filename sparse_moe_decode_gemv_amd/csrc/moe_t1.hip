@@ -374,33 +374,41 @@ struct GateUp {
   }
 };
 
-// Tasks first, first + stride, ... below ntask; the first task's weights are
-// already in (ca, sa) (requested by the caller ahead of the x staging).  Task
-// i + 1 is requested before task i is reduced.  The loop runs an exact trip
-// count and the last one or two tasks are peeled, so no load sits under a
-// branch that rejoins: at such a join the compiler's wait counts assume the
-// path without the load and would wait for the newer loads as well.
+// A wave's task list: first + i * stride for i < n1, then first2 + (i - n1)
+// * stride2 up to n tasks in all.
+struct TaskSeq {
+  int first, stride, n1, first2, stride2, n;
+  __device__ __forceinline__ int at(int i) const {
+    return i < n1 ? first + i * stride : first2 + (i - n1) * stride2;
+  }
+};
+
+// The tasks of q in order; the first task's weights are already in (ca, sa)
+// (requested by the caller ahead of the x staging).  Task i + 1 is requested
+// before task i is reduced.  The loop runs an exact trip count and the last
+// one or two tasks are peeled, so no load sits under a branch that rejoins:
+// at such a join the compiler's wait counts assume the path without the load
+// and would wait for the newer loads as well.
 template <int BPL, int LANES>
 __device__ void gateup_tasks(const GateUp<BPL, LANES>& g, const GateUpJob& J, const uint32_t* x_lds,
-                             int ntask, int first, int stride, uint4 (&ca)[BPL],
-                             uint32_t (&sa)[BPL]) {
-  if (first >= ntask) return;
-  const int n = (ntask - first + stride - 1) / stride;
+                             const TaskSeq& q, uint4 (&ca)[BPL], uint32_t (&sa)[BPL]) {
+  const int n = q.n;
+  if (n <= 0) return;
   uint4 cb[BPL];
   uint32_t sb[BPL];
-  int t = first, i = 0;
-  for (; i + 2 < n; i += 2, t += 2 * stride) {
-    g.load(J, t + stride, cb, sb);
-    g.finish(J, x_lds, t, ca, sa);
-    g.load(J, t + 2 * stride, ca, sa);
-    g.finish(J, x_lds, t + stride, cb, sb);
+  int i = 0;
+  for (; i + 2 < n; i += 2) {
+    g.load(J, q.at(i + 1), cb, sb);
+    g.finish(J, x_lds, q.at(i), ca, sa);
+    g.load(J, q.at(i + 2), ca, sa);
+    g.finish(J, x_lds, q.at(i + 1), cb, sb);
   }
   if (n - i == 2) {
-    g.load(J, t + stride, cb, sb);
-    g.finish(J, x_lds, t, ca, sa);
-    g.finish(J, x_lds, t + stride, cb, sb);
+    g.load(J, q.at(i + 1), cb, sb);
+    g.finish(J, x_lds, q.at(i), ca, sa);
+    g.finish(J, x_lds, q.at(i + 1), cb, sb);
   } else {
-    g.finish(J, x_lds, t, ca, sa);
+    g.finish(J, x_lds, q.at(i), ca, sa);
   }
 }
 
@@ -456,6 +464,7 @@ __global__ __launch_bounds__(kBlock) void k1_topk(LayerT1 L) {
 // Two waves per SIMD for the gate/up kernel: three (at most 168 registers)
 // measured no faster, and the selection then covers fewer shared tasks.
 constexpr int kK2WavesPerSimd = 2;
+constexpr int kK2OldRounds = 2;  // task rounds given to the older workgroups only
 
 // K2: gate/up of the shared expert and of the k selected experts.  With
 // idx == null the experts are selected here: every workgroup runs the same
@@ -519,7 +528,21 @@ __global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, 
     if (L.idx_out) L.idx_out[threadIdx.x] = e;
     if (L.w_out) L.w_out[threadIdx.x] = w;
   }
-  gateup_tasks(g, J, x_lds, ntask, first, gridDim.x * kWaves, ca, sa);
+  // Rounds of one task per wave, except that the last kK2OldRounds rounds
+  // go to the older half of the workgroups (launched first: on each CU the
+  // older workgroup's waves are served first and would otherwise finish
+  // early, leaving the younger ones streaming with half the loads in flight).
+  const int nw = gridDim.x * kWaves, rounds = ntask / nw;
+  TaskSeq q{first, nw, 0, 0, nw / 2, 0};
+  if (rounds >= 8) {
+    const int split = (rounds - kK2OldRounds) * nw;
+    q.n1 = rounds - kK2OldRounds;
+    q.first2 = split + first;
+    q.n = q.n1 + (first < nw / 2 && q.first2 < ntask ? (ntask - q.first2 + nw / 2 - 1) / (nw / 2) : 0);
+  } else {
+    q.n1 = q.n = first < ntask ? (ntask - first + nw - 1) / nw : 0;
+  }
+  gateup_tasks(g, J, x_lds, q, ca, sa);
 }
 
 // K3: down projection of every slot on the matrix cores, router-weighted

@@ -26,8 +26,8 @@ constexpr int kTopkBlock = 256;
 constexpr int kTopkPerThread = kMaxExperts / kTopkBlock;  // keys per thread
 
 struct TopkLds {
-  uint32_t cand_key[kWave];  // wave top-k: compacted candidates
-  int32_t cand_idx[kWave];
+  alignas(16) uint32_t lmax[kWave];  // wave top-k: lane maxima
+  uint64_t cand[2 * kWave];          // candidates; the upper half takes discarded stores
   uint32_t hist[kTopkBlock / kWave][256];  // one histogram per wave
   uint32_t sel_key[kMaxTopK];
   int32_t sel_idx[kMaxTopK];
@@ -150,65 +150,91 @@ __device__ inline void topk_softmax_block(const float (&lg)[kTopkPerThread], int
   }
 }
 
+// Sum over the 64 lanes by DPP within rows, then the four row sums (the same
+// order in every wave, so every workgroup gets the same weights).
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Top-k + softmax by ONE wave, without barriers (E <= 1024, k <= 32).  Lane l
 // holds experts 16 l .. 16 l + 15 as order-preserving keys (key[m], 0 for an
 // absent expert); the order is the block version's: larger logit first,
-// lower index first among equal logits.
-//  1. T = the k-th largest of the 64 lane maxima (lanes ranked by (key,
-//     lane)): at least k keys are >= T, so every selected key is.
-//  2. The present keys >= T (C of them, C >= k; about k + 2 for random
-//     logits) are compacted in expert order into S.cand_* by a wave scan.
-//  3. Candidate j (lane j) is ranked against the others by (key desc, index
-//     asc); ranks below k are the selection, written in that order with
-//     their softmax weights.
+// lower index first among equal logits.  Every step is a few independent
+// compares per lane (LDS broadcast reads), not a chain of cross-lane reads.
+//  1. T = the k-th largest of the 64 lane maxima: a lane's maximum is T when
+//     at least k lane maxima are >= it and it is the largest such.  At least
+//     k keys are >= T, so every selected key is.
+//  2. The present keys >= T (C of them, C >= k; about k + 3 for random
+//     logits) are compacted into S.cand as 64-bit composites key << 32 |
+//     ~index, which order the experts exactly as the selection does (a
+//     larger composite ranks first; composites are distinct).  Entries C ..
+//     63 are zero, below every candidate.
+//  3. Candidate j (lane j) counts the composites above its own: its rank.
+//     Ranks below k are the selection, written in that order with their
+//     softmax weights.
 // Returns false, writing nothing, when C > 64 (only with many equal logits
-// at the threshold); the caller then runs topk_softmax_wave_rounds.
+// at the threshold, or E > 64 with fewer than k lanes holding experts); the
+// caller then runs topk_softmax_wave_rounds.
 __device__ inline bool topk_softmax_wave(const uint32_t (&key)[16], int E, int k, TopkLds& S,
                                          int32_t* idx, float* wts, int32_t* idx_out, float* w_out) {
   const int lane = threadIdx.x & 63;
-  // 1. lane maximum (the first of equal keys: the lower index) and its rank
+  const int base = lane * 16;
+  // 1. threshold
   uint32_t lm = 0u;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) lm = key[m] > lm ? key[m] : lm;
-  int rank = 0;
-  for (int j = 0; j < kWave; ++j) {
-    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)lm, j);
-    rank += (kj > lm || (kj == lm && j < lane)) ? 1 : 0;
-  }
-  const uint64_t at = __ballot(rank == k - 1);
-  const uint32_t T = (uint32_t)__builtin_amdgcn_readlane((int)lm, (int)__builtin_ctzll(at));
-  // 2. present keys >= T, compacted in expert order
-  const int base = lane * 16;
+  for (int m = 0; m < 16; ++m) lm = umax32(lm, key[m]);
+  S.lmax[lane] = lm;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  uint32_t ge[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < kWave; ++j) ge[j & 3] += S.lmax[j] >= lm ? 1u : 0u;
+  const uint32_t T = wave_max_u32((ge[0] + ge[1]) + (ge[2] + ge[3]) >= (uint32_t)k ? lm : 0u);
+  // 2. compaction (every lane stores 16 times; non-candidates into the upper half)
+  bool take[16];
   uint32_t cnt = 0u;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) cnt += (base + m < E && key[m] >= T) ? 1u : 0u;
+  for (int m = 0; m < 16; ++m) {
+    take[m] = base + m < E && key[m] >= T;
+    cnt += take[m] ? 1u : 0u;
+  }
   const uint32_t incl = wave_incl_scan_u32(cnt);
   const int C = __builtin_amdgcn_readlane((int)incl, kWave - 1);
   if (C > kWave) return false;
   uint32_t pos = incl - cnt;
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
-    if (base + m < E && key[m] >= T) {
-      S.cand_key[pos] = key[m];
-      S.cand_idx[pos] = base + m;
-      ++pos;
-    }
+    const uint32_t p = take[m] ? pos : (uint32_t)(kWave + lane);
+    S.cand[p] = ((uint64_t)key[m] << 32) | (uint64_t)(~(uint32_t)(base + m));
+    pos += take[m] ? 1u : 0u;
   }
+  if (lane >= C) S.cand[lane] = 0ull;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  const bool act = lane < C;
-  const uint32_t ck = act ? S.cand_key[lane] : 0u;
-  const int ci = act ? S.cand_idx[lane] : 0;
-  // 3. exact rank among the candidates
-  int r = 0;
-  for (int j = 0; j < C; ++j) {
-    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ck, j);
-    const int ij = __builtin_amdgcn_readlane(ci, j);
-    r += (kj > ck || (kj == ck && ij < ci)) ? 1 : 0;
+  // 3. ranks
+  const uint64_t mine = S.cand[lane];
+  uint32_t rk[4] = {0u, 0u, 0u, 0u};
+  if (C <= kWave / 2) {
+#pragma unroll
+    for (int j = 0; j < kWave / 2; ++j) rk[j & 3] += S.cand[j] > mine ? 1u : 0u;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWave; ++j) rk[j & 3] += S.cand[j] > mine ? 1u : 0u;
   }
-  const bool sel = act && r < k;
-  const uint32_t top = wave_max_u32(sel ? ck : 0u);
+  const int r = (int)((rk[0] + rk[1]) + (rk[2] + rk[3]));
+  const bool sel = lane < C && r < k;
+  const uint32_t ck = (uint32_t)(mine >> 32);
+  const int ci = (int)~(uint32_t)mine;
+  const uint64_t first = __ballot(sel && r == 0);  // exactly one lane: the largest logit
+  const uint32_t top = (uint32_t)__builtin_amdgcn_readlane((int)ck, (int)__builtin_ctzll(first));
   const float ex = sel ? expf(f32_from_order_key(ck) - f32_from_order_key(top)) : 0.f;
-  const float sum = wave_sum(ex);
+  const float sum = wave_sum_rows(ex);
   if (sel) {
     const float w = ex / sum;
     idx[r] = ci;
