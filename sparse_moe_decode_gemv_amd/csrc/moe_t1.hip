@@ -470,17 +470,27 @@ constexpr int kK2OldRounds = 2;  // task rounds given to the older workgroups on
 // idx == null the experts are selected here: every workgroup runs the same
 // top-k on the router logits (deterministic, identical in every workgroup)
 // and workgroup 0 publishes the indices and weights for K3 and the caller.
-// With a shared expert (PRE) a wave whose first task is a shared one
-// requests it before the selection, so the selection latency is spent under
-// shared-expert bytes.
-template <int BPLH, int LANES, bool PRE>
-__global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, const uint16_t* __restrict__ x,
-                                                    const int32_t* __restrict__ idx,
-                                                    float* __restrict__ act, int gu_lanes, int ns) {
-  __shared__ __align__(16) uint32_t x_lds[kMaxH / 2];
-  __shared__ int32_t e_lds[kMaxTopK];
-  __shared__ float w_lds[kMaxTopK];
-  __shared__ TopkLds tk;
+// With a shared expert (PRE) the workgroups whose waves all start on a
+// shared task (the first ns / 4) request it before the selection, so the
+// selection latency is spent under shared-expert bytes; the others (when
+// the expert is narrower than the grid has waves) request their first task
+// after it.  The two kinds are separate code paths chosen per workgroup, so
+// neither has a load under a branch that rejoins.
+struct K2Lds {
+  uint32_t x[kMaxH / 2];
+  int32_t e[kMaxTopK];
+  float w[kMaxTopK];
+  TopkLds tk;
+};
+
+template <int BPLH, int LANES, bool EARLY>
+__device__ __forceinline__ void k2_body(const LayerT1& L, const uint16_t* __restrict__ x,
+                                        const int32_t* __restrict__ idx, float* __restrict__ act,
+                                        int gu_lanes, int ns, K2Lds& sm) {
+  uint32_t* x_lds = sm.x;
+  int32_t* e_lds = sm.e;
+  float* w_lds = sm.w;
+  TopkLds& tk = sm.tk;
   const int wid = wave_id();
   const GateUpJob J{L.g_codes,  L.g_scales,  L.u_codes,  L.u_scales, L.sg_codes, L.sg_scales,
                     L.su_codes, L.su_scales, e_lds,      L.H,        L.F,        L.k,
@@ -503,7 +513,7 @@ __global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, 
   stage_x_load(x, L.H, xs);
   uint4 ca[BPLH];
   uint32_t sa[BPLH];
-  constexpr bool early = PRE;  // the launcher gives every wave a shared first task
+  constexpr bool early = EARLY;  // every wave of this workgroup starts on a shared task
   if (early) g.load(J, first, ca, sa);
   if (idx) {
     if (threadIdx.x < L.k)
@@ -543,6 +553,17 @@ __global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, 
     q.n1 = q.n = first < ntask ? (ntask - first + nw - 1) / nw : 0;
   }
   gateup_tasks(g, J, x_lds, q, ca, sa);
+}
+
+template <int BPLH, int LANES, bool PRE>
+__global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, const uint16_t* __restrict__ x,
+                                                    const int32_t* __restrict__ idx,
+                                                    float* __restrict__ act, int gu_lanes, int ns) {
+  __shared__ __align__(16) K2Lds sm;
+  if (PRE && (int)blockIdx.x < ns / kWaves)  // workgroup-uniform
+    k2_body<BPLH, LANES, true>(L, x, idx, act, gu_lanes, ns, sm);
+  else
+    k2_body<BPLH, LANES, false>(L, x, idx, act, gu_lanes, ns, sm);
 }
 
 // K3: down projection of every slot on the matrix cores, router-weighted
@@ -978,11 +999,15 @@ hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* 
   const int ns = (with_shared && L.S) ? tps : 0;
   const int tasks = ns + L.k * tps;
   const int cap = kNumCU * kK2WavesPerCU / kWaves;
-  int n_gu = ceil_div(tasks, kWaves * 4) < cap ? ceil_div(tasks, kWaves * 4) : cap;
-  // with a shared expert every wave starts on a shared task (tps is a
-  // multiple of kWaves for every accepted F), requested before the selection
+  // about four tasks per wave where there are enough, else one per wave on
+  // as many workgroups as the chip holds (narrow experts: latency-bound)
+  int n_gu = ceil_div(tasks, kWaves * 4);
+  if (n_gu < cap) n_gu = ceil_div(tasks, kWaves) < cap ? ceil_div(tasks, kWaves) : cap;
+  if (n_gu > cap) n_gu = cap;
+  // with a shared expert the first ns / kWaves workgroups start on shared
+  // tasks (tps is a multiple of kWaves for every accepted F), requested
+  // before the selection
   const bool pre = ns > 0;
-  if (pre && n_gu * kWaves > ns) n_gu = ns / kWaves;
   switch (gm.bpl) {
     case 1: return k2_launch<1>(L, x, idx, act, n_gu, gm.lanes, ns, pre, s);
     case 2: return k2_launch<2>(L, x, idx, act, n_gu, gm.lanes, ns, pre, s);

@@ -2,7 +2,10 @@
 
   python -m sparse_moe_decode_gemv_amd.profiling trace <run_results.db | kernel_trace.csv>
       per-kernel launch count and duration (mean / median / min), each
-      gate/up launch classed as in-layer (after the router) or stand-alone.
+      gate/up launch classed as in-layer (after the router) or stand-alone;
+      then per decode layer (router .. combine, launched back to back) the
+      kernel count, the span from the first start to the last end, the idle
+      time between the layer's kernels and the gap to the next layer.
 
   python -m sparse_moe_decode_gemv_amd.profiling counters <fetch.csv> <write.csv>
       HBM bytes per launch from two counter-collection runs (FETCH_SIZE, then
@@ -73,6 +76,51 @@ def trace(path: str) -> str:
     out = [f"{'kernel':28s} {'launches':>8s} {'mean us':>9s} {'median':>9s} {'min':>9s}"]
     for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
         out.append(f"{k:28s} {len(v):8d} {st.mean(v):9.2f} {st.median(v):9.2f} {min(v):9.2f}")
+    out += ["", layer_spans(names, rows)]
+    return "\n".join(out)
+
+
+_FIRST = ("k1_router", "kb_rmsnorm", "kb_router")
+_LAST = ("k3_slab", "k3_down", "kb_combine")
+
+
+def layer_spans(names, rows) -> str:
+    """Decode layers as launched: a layer opens with the router (or the
+    batched RMSNorm before it) and closes with the down/combine kernel, with
+    only layer kernels in between.  Times in microseconds."""
+    layers, cur = [], None
+    for n, r in zip(names, rows):
+        opens = n in _FIRST and not (n == "kb_router" and cur and cur[-1][0] == "kb_rmsnorm")
+        if opens:
+            cur = [(n, r[1], r[2])]
+        elif cur is not None:
+            if n.startswith(("k1_", "k2_", "k3_", "kb_")):
+                cur.append((n, r[1], r[2]))
+            else:
+                cur = None
+                continue
+        if cur is not None and n in _LAST:
+            layers.append(cur)
+            cur = None
+    if not layers:
+        return "no complete decode layer in the trace"
+    spans = [(l[-1][2] - l[0][1]) / 1e3 for l in layers]
+    idle = [sum(max(0, b[1] - a[2]) for a, b in zip(l, l[1:])) / 1e3 for l in layers]
+    nk = collections.Counter(len(l) for l in layers)
+    between = [(b[0][1] - a[-1][2]) / 1e3 for a, b in zip(layers, layers[1:])
+               if 0 <= b[0][1] - a[-1][2] < 50_000]
+    seqs = collections.Counter(" > ".join(k[0] for k in l) for l in layers)
+    out = [f"decode layers in the trace: {len(layers)}; kernels per layer: "
+           + ", ".join(f"{k} ({v} layers)" for k, v in sorted(nk.items())),
+           f"layer span (first start .. last end) us: mean {st.mean(spans):.2f} "
+           f"median {st.median(spans):.2f} min {min(spans):.2f}",
+           f"idle between a layer's kernels us: mean {st.mean(idle):.2f} "
+           f"median {st.median(idle):.2f} max {max(idle):.2f}"]
+    if between:
+        out.append(f"gap to the next layer us: mean {st.mean(between):.2f} "
+                   f"median {st.median(between):.2f}")
+    for s_, c in seqs.most_common(3):
+        out.append(f"  {c:5d} x {s_}")
     return "\n".join(out)
 
 
