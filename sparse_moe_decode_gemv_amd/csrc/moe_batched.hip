@@ -228,27 +228,20 @@ __device__ __forceinline__ int token_of(const LayerTB& L, int pid) {
 // four waves share the group's tokens: per K chunk of KC elements the
 // workgroup stages 16 tokens' activations in LDS (rows padded by 16 bytes so
 // that the 16 lanes of a ds_read_b128 phase hit distinct banks), double
-// buffered; each wave streams its own 16 gate and 16 up rows one chunk ahead
-// in registers (two statically named register sets).
+// buffered; each wave streams its own 16 gate and 16 up rows in registers
+// (two statically named register sets).
+//
+// Pipeline of chunk c (one barrier per chunk): products of chunk c, then
+// the requests for chunk c + 2 (token activations into staging registers,
+// then weights into the set chunk c used), then chunk c + 1's activations,
+// requested one chunk earlier, go to LDS.  Scheduling fences keep the
+// requests in this order (the wait counter completes them in order).  Every wait is thus for requests
+// a whole chunk old, never for the ones just issued.  Requests past the
+// last chunk re-read the last one (in bounds, unused), so that no load sits
+// under a branch.
 template <int KC>
 struct TokLds {
   uint4 b[2][16][KC / 8 + 1];
-};
-
-// Up to two staged uint4 per thread and chunk, held in named registers.
-template <int PER>
-struct Stage {
-  u32x4 v0, v1;
-  __device__ __forceinline__ void load(const uint4* src) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(src);
-    v0 = p[0];
-    if (PER > 1) v1 = p[1];
-  }
-  __device__ __forceinline__ void store(uint4* dst) const {
-    u32x4* p = reinterpret_cast<u32x4*>(dst);
-    p[0] = v0;
-    if (PER > 1) p[1] = v1;
-  }
 };
 
 template <int KC>
@@ -257,17 +250,64 @@ struct GuRegs {
   uint32_t sg[KC / 128], su[KC / 128];
 };
 
+// A wave's 16-row MXFP4 weight tile: codes [16][rowc bytes] and scales
+// [16][rows bytes] from wave-uniform bases (lane r reads row r).  Every
+// request uses a per-lane offset fixed for the whole tile plus the chunk's
+// position as a scalar offset, so no address register is rebuilt (or
+// overwritten by a load) inside the chunk loop.  A request past the last
+// chunk goes through an empty descriptor: the instruction is issued (so the
+// wait counts stay exact) but touches no memory.
+struct Tile {
+  const uint8_t *c, *s;
+  uint32_t rowc, rows;
+};
+__device__ __forceinline__ Tile make_tile(const uint8_t* codes, const uint8_t* scales, size_t row0,
+                                          int K) {
+  // the first row is wave-uniform: keep the bases in scalar registers
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)row0);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(row0 >> 32));
+  const size_t r0 = ((size_t)hi << 32) | lo;
+  return {codes + r0 * (size_t)(K / 2), scales + r0 * (size_t)(K / 32), (uint32_t)K / 2, (uint32_t)K / 32};
+}
+
 template <int KC>
-__device__ __forceinline__ void gu_load_a(GuRegs<KC>& R, const uint8_t* gc, const uint8_t* gs,
-                                          const uint8_t* uc, const uint8_t* us, int c, int q) {
+__device__ __forceinline__ void ld_tile(uint4 (&a)[KC / 128], uint32_t (&sc)[KC / 128], const Tile& T,
+                                        uint32_t voc, uint32_t vos, int c, int nch) {
+  const bool live = c < nch;
+  const uint32_t cc = (uint32_t)(live ? c : nch - 1);
+  const auto rc = buf_rsrc(T.c, live ? 16u * T.rowc : 0u), rs = buf_rsrc(T.s, live ? 16u * T.rows : 0u);
+  const uint32_t soc = cc * (KC / 2), sos = cc * (KC / 32);
 #pragma unroll
-  for (int kk = 0; kk < KC / 128; ++kk) {
-    const int blk = c * (KC / 32) + kk * 4 + q;
-    R.ag[kk] = ld_stream16(gc + (size_t)blk * 16);
-    R.au[kk] = ld_stream16(uc + (size_t)blk * 16);
-    R.sg[kk] = ld_stream8(gs + blk);
-    R.su[kk] = ld_stream8(us + blk);
+  for (int kk = 0; kk < KC / 128; ++kk) {  // block cc * KC / 32 + 4 kk + q of row r
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(voc + 64u * kk), (int)soc, kBufNT);
+    a[kk] = make_uint4(v[0], v[1], v[2], v[3]);
+    sc[kk] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)(vos + 4u * kk), (int)sos, kBufNT);
   }
+}
+
+// Token-activation staging: PER 16-byte pieces per thread from a row of a
+// bf16 array (one descriptor over the whole array, the row and piece as a
+// fixed per-thread offset, the chunk as a scalar offset).
+template <int PER>
+struct Stage {
+  u32x4 v[PER];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 16u * i), (int)soff, 0));
+  }
+  __device__ __forceinline__ void store(uint4* dst) const {
+    u32x4* p = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) p[i] = v[i];
+  }
+};
+
+template <int KC>
+__device__ __forceinline__ void gu_load_a(GuRegs<KC>& R, const Tile& G, const Tile& U, uint32_t voc,
+                                          uint32_t vos, int c, int nch) {
+  ld_tile<KC>(R.ag, R.sg, G, voc, vos, c, nch);
+  ld_tile<KC>(R.au, R.su, U, voc, vos, c, nch);
 }
 
 template <int KC>
@@ -285,7 +325,11 @@ __device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, const uint4 (*bt)[KC
   }
 }
 
-template <int KC>
+// NCH > 0: the chunk count (H / KC) fixed at compile time; the chunk loop
+// is then unrolled whole, so that the wait counts carry no loop back-edge
+// merge (with one, the compiler's waits become conservative and every chunk
+// waits for the requests just issued).
+template <int KC, int NCH>
 __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
   __shared__ TokLds<KC> S;
   constexpr int PER = KC / 128;  // staged uint4 per thread per chunk
@@ -293,45 +337,60 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
   const int ng = L.ginfo[0];
   const int quads = L.F / (kTileRows * kWv);
   const int nitems = ng * quads;
-  const int nch = L.H / KC;
+  const int nch = NCH ? NCH : L.H / KC;
   const int sc = tid >> 4, sj = (tid & 15) * PER;  // staging: token row, first uint4
+  const auto rx = buf_rsrc(L.x, (uint32_t)L.T * (uint32_t)L.H * 2u);
   for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
     const int g = it / quads, rq = it - g * quads;
     const int e = L.g_expert[g], start = L.g_start[g], m = L.g_count[g];
     const bool sh = e >= L.E;
-    const int row = (rq * kWv + wid) * kTileRows + r;
-    const size_t rsel = (sh ? 0 : (size_t)e * L.F) + row;
-    const uint8_t* gc = (sh ? L.sg_codes : L.g_codes) + rsel * (L.H / 2);
-    const uint8_t* gs = (sh ? L.sg_scales : L.g_scales) + rsel * (L.H / 32);
-    const uint8_t* uc = (sh ? L.su_codes : L.u_codes) + rsel * (L.H / 2);
-    const uint8_t* us = (sh ? L.su_scales : L.u_scales) + rsel * (L.H / 32);
+    const size_t row0 = (sh ? 0 : (size_t)e * L.F) + (size_t)(rq * kWv + wid) * kTileRows;
+    const Tile G = make_tile(sh ? L.sg_codes : L.g_codes, sh ? L.sg_scales : L.g_scales, row0, L.H);
+    const Tile U = make_tile(sh ? L.su_codes : L.u_codes, sh ? L.su_scales : L.u_scales, row0, L.H);
+    const uint32_t voc = (uint32_t)r * G.rowc + 16u * (uint32_t)q, vos = (uint32_t)r * G.rows + (uint32_t)q;
     for (int n0 = 0; n0 < m; n0 += 16) {
       const int cs = n0 + sc < m ? n0 + sc : m - 1;
-      const uint4* xs = reinterpret_cast<const uint4*>(
-          L.x + (size_t)token_of(L, L.order[start + cs]) * L.H);
+      const uint32_t xvo = (uint32_t)token_of(L, L.order[start + cs]) * (uint32_t)L.H * 2u + 16u * (uint32_t)sj;
+      auto xso = [&](int c) { return (uint32_t)(c < nch ? c : nch - 1) * (uint32_t)(KC * 2); };
       f32x4 cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
       GuRegs<KC> A0, A1;
-      Stage<PER> bst;
-      gu_load_a<KC>(A0, gc, gs, uc, us, 0, q);
-      bst.load(xs + sj);
-      bst.store(&S.b[0][sc][sj]);
+      Stage<PER> xa, xb;
+      xa.load(rx, xvo, xso(0));
+      __builtin_amdgcn_sched_barrier(0);
+      gu_load_a<KC>(A0, G, U, voc, vos, 0, nch);
+      __builtin_amdgcn_sched_barrier(0);
+      xb.load(rx, xvo, xso(1));
+      __builtin_amdgcn_sched_barrier(0);
+      gu_load_a<KC>(A1, G, U, voc, vos, 1, nch);
+      __builtin_amdgcn_sched_barrier(0);
+      xa.store(&S.b[0][sc][sj]);
       __syncthreads();
-      for (int c = 0; c < nch; c += 2) {
-        if (c + 1 < nch) {
-          gu_load_a<KC>(A1, gc, gs, uc, us, c + 1, q);
-          bst.load(xs + (size_t)(c + 1) * (KC / 8) + sj);
+      // chunk c: weights in Ac, activations in LDS buffer bu; chunk c + 1's
+      // weights and activations (xs) in flight; xl takes chunk c + 2's
+      auto step = [&](int c, GuRegs<KC>& Ac, Stage<PER>& xl, const Stage<PER>& xs,
+                      const uint4 (*bu)[KC / 8 + 1], uint4 (*bs)[KC / 8 + 1]) {
+        gu_mma<KC>(Ac, bu, q, r, cg, cu);
+        if (!NCH || c + 2 < nch) {
+          xl.load(rx, xvo, xso(c + 2));
+          __builtin_amdgcn_sched_barrier(0);
+          gu_load_a<KC>(Ac, G, U, voc, vos, c + 2, nch);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        gu_mma<KC>(A0, S.b[0], q, r, cg, cu);
-        if (c + 1 < nch) bst.store(&S.b[1][sc][sj]);
+        if (!NCH || c + 1 < nch) xs.store(&bs[sc][sj]);
         __syncthreads();
-        if (c + 1 >= nch) break;
-        if (c + 2 < nch) {
-          gu_load_a<KC>(A0, gc, gs, uc, us, c + 2, q);
-          bst.load(xs + (size_t)(c + 2) * (KC / 8) + sj);
+      };
+      if constexpr (NCH > 0) {
+#pragma unroll
+        for (int c = 0; c < NCH; c += 2) {
+          step(c, A0, xa, xb, S.b[0], S.b[1]);
+          if (c + 1 < NCH) step(c + 1, A1, xb, xa, S.b[1], S.b[0]);
         }
-        gu_mma<KC>(A1, S.b[1], q, r, cg, cu);
-        if (c + 2 < nch) bst.store(&S.b[0][sc][sj]);
-        __syncthreads();
+      } else {
+        for (int c = 0; c < nch; c += 2) {
+          step(c, A0, xa, xb, S.b[0], S.b[1]);
+          if (c + 1 >= nch) break;
+          step(c + 1, A1, xb, xa, S.b[1], S.b[0]);
+        }
       }
       if (n0 + r < m) {
         const size_t o = (size_t)(start + n0 + r) * L.F + (rq * kWv + wid) * kTileRows + 4 * q;
@@ -357,7 +416,8 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
 // ---------------------------------------------------------------- down
 // Workgroup items (group, kDnWaves consecutive 16-row tiles of the hidden
 // size); per K chunk the workgroup stages the 16 pairs' a_hi and a_lo in LDS
-// (double buffered) and each wave streams its 16 down rows one chunk ahead.
+// (double buffered) and each wave streams its 16 down rows, pipelined as in
+// the gate/up kernel (waits only for requests a chunk old).
 constexpr int kDnWaves = 8;
 constexpr int kDnBlock = kDnWaves * kWave;
 
@@ -368,14 +428,9 @@ struct DnRegs {
 };
 
 template <int KC>
-__device__ __forceinline__ void dn_load_a(DnRegs<KC>& R, const uint8_t* dc, const uint8_t* ds, int c,
-                                          int q) {
-#pragma unroll
-  for (int kk = 0; kk < KC / 128; ++kk) {
-    const int blk = c * (KC / 32) + kk * 4 + q;
-    R.a[kk] = ld_stream16(dc + (size_t)blk * 16);
-    R.sc[kk] = ld_stream8(ds + blk);
-  }
+__device__ __forceinline__ void dn_load_a(DnRegs<KC>& R, const Tile& D, uint32_t voc, uint32_t vos, int c,
+                                          int nch) {
+  ld_tile<KC>(R.a, R.sc, D, voc, vos, c, nch);
 }
 
 template <int KC>
@@ -393,7 +448,7 @@ __device__ __forceinline__ void dn_mma(const DnRegs<KC>& R, const uint4 (*bh)[KC
   }
 }
 
-template <int KC>
+template <int KC, int NCH>
 __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
   __shared__ TokLds<KC> Sh, Sl;
   constexpr int PER = KC / 128;
@@ -401,46 +456,63 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
   const int ng = L.ginfo[0];
   const int slabs = L.H / (kTileRows * kDnWaves);
   const int nitems = ng * slabs;
-  const int nch = L.F / KC;
+  const int nch = NCH ? NCH : L.F / KC;
   const bool st_lo = tid >= 256;  // staging: threads 0..255 stage a_hi, 256..511 a_lo
   const int sc = (tid & 255) >> 4, sj = (tid & 15) * PER;
+  // staged pairs: a_hi (threads 0..255) or a_lo (256..511), [pairs][F] bf16
+  const uint32_t npairs = (uint32_t)(L.T * L.k + L.S * L.T);
+  const auto ra = buf_rsrc(st_lo ? L.act_lo : L.act_hi, npairs * (uint32_t)L.F * 2u);
   for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
     const int g = it / slabs, sb = it - g * slabs;
     const int e = L.g_expert[g], start = L.g_start[g], m = L.g_count[g];
     const bool sh = e >= L.E;
     const int rt = sb * kDnWaves + wid;
-    const size_t rsel = (sh ? 0 : (size_t)e * L.H) + rt * kTileRows + r;
-    const uint8_t* dc = (sh ? L.sd_codes : L.d_codes) + rsel * (L.F / 2);
-    const uint8_t* ds = (sh ? L.sd_scales : L.d_scales) + rsel * (L.F / 32);
+    const size_t row0 = (sh ? 0 : (size_t)e * L.H) + (size_t)rt * kTileRows;
+    const Tile D = make_tile(sh ? L.sd_codes : L.d_codes, sh ? L.sd_scales : L.d_scales, row0, L.F);
+    const uint32_t voc = (uint32_t)r * D.rowc + 16u * (uint32_t)q, vos = (uint32_t)r * D.rows + (uint32_t)q;
     for (int n0 = 0; n0 < m; n0 += 16) {
       const int cs = n0 + sc < m ? n0 + sc : m - 1;
-      const uint4* as = reinterpret_cast<const uint4*>((st_lo ? L.act_lo : L.act_hi) +
-                                                       (size_t)(start + cs) * L.F);
+      const uint32_t xvo = (uint32_t)(start + cs) * (uint32_t)L.F * 2u + 16u * (uint32_t)sj;
+      auto xso = [&](int c) { return (uint32_t)(c < nch ? c : nch - 1) * (uint32_t)(KC * 2); };
       uint4 (*sbuf0)[KC / 8 + 1] = st_lo ? Sl.b[0] : Sh.b[0];
       uint4 (*sbuf1)[KC / 8 + 1] = st_lo ? Sl.b[1] : Sh.b[1];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       DnRegs<KC> A0, A1;
-      Stage<PER> bst;
-      dn_load_a<KC>(A0, dc, ds, 0, q);
-      bst.load(as + sj);
-      bst.store(&sbuf0[sc][sj]);
+      Stage<PER> xa, xb;
+      xa.load(ra, xvo, xso(0));
+      __builtin_amdgcn_sched_barrier(0);
+      dn_load_a<KC>(A0, D, voc, vos, 0, nch);
+      __builtin_amdgcn_sched_barrier(0);
+      xb.load(ra, xvo, xso(1));
+      __builtin_amdgcn_sched_barrier(0);
+      dn_load_a<KC>(A1, D, voc, vos, 1, nch);
+      __builtin_amdgcn_sched_barrier(0);
+      xa.store(&sbuf0[sc][sj]);
       __syncthreads();
-      for (int c = 0; c < nch; c += 2) {
-        if (c + 1 < nch) {
-          dn_load_a<KC>(A1, dc, ds, c + 1, q);
-          bst.load(as + (size_t)(c + 1) * (KC / 8) + sj);
+      auto step = [&](int c, DnRegs<KC>& Ac, Stage<PER>& xl, const Stage<PER>& xs, int bu,
+                      uint4 (*bs)[KC / 8 + 1]) {
+        dn_mma<KC>(Ac, Sh.b[bu], Sl.b[bu], q, r, acc);
+        if (!NCH || c + 2 < nch) {
+          xl.load(ra, xvo, xso(c + 2));
+          __builtin_amdgcn_sched_barrier(0);
+          dn_load_a<KC>(Ac, D, voc, vos, c + 2, nch);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        dn_mma<KC>(A0, Sh.b[0], Sl.b[0], q, r, acc);
-        if (c + 1 < nch) bst.store(&sbuf1[sc][sj]);
+        if (!NCH || c + 1 < nch) xs.store(&bs[sc][sj]);
         __syncthreads();
-        if (c + 1 >= nch) break;
-        if (c + 2 < nch) {
-          dn_load_a<KC>(A0, dc, ds, c + 2, q);
-          bst.load(as + (size_t)(c + 2) * (KC / 8) + sj);
+      };
+      if constexpr (NCH > 0) {
+#pragma unroll
+        for (int c = 0; c < NCH; c += 2) {
+          step(c, A0, xa, xb, 0, sbuf1);
+          if (c + 1 < NCH) step(c + 1, A1, xb, xa, 1, sbuf0);
         }
-        dn_mma<KC>(A1, Sh.b[1], Sl.b[1], q, r, acc);
-        if (c + 2 < nch) bst.store(&sbuf0[sc][sj]);
-        __syncthreads();
+      } else {
+        for (int c = 0; c < nch; c += 2) {
+          step(c, A0, xa, xb, 0, sbuf1);
+          if (c + 1 >= nch) break;
+          step(c + 1, A1, xb, xa, 1, sbuf0);
+        }
       }
       if (n0 + r < m) {
         float4 v;
@@ -564,7 +636,8 @@ __global__ __launch_bounds__(kBlk) void kb_rmsnorm(const uint16_t* __restrict__ 
   }
 }
 
-constexpr int kGroupedBlocksPerCU = 4;
+constexpr int kGroupedBlocksPerCU = 4;  // 256-element chunks (93 registers)
+constexpr int kGroupedBlocksPerCU512 = 3;  // 512-element chunks: 157 registers, 3 waves per SIMD
 constexpr int kDownBlocksPerCU = 2;
 constexpr int kNumCUs = 256;
 
@@ -588,17 +661,30 @@ hipError_t launch_group_tb(const LayerTB& L, hipStream_t s) {
 }
 
 hipError_t launch_gateup_tb(const LayerTB& L, hipStream_t s) {
-  // H % 256 == 0 always; 256-element chunks
-  hipLaunchKernelGGL(kb_gateup<256>, dim3(kNumCUs * kGroupedBlocksPerCU), dim3(kBlk), 0, s, L);
+  // H % 256 == 0 always; 512-element chunks where they divide H
+  // every workgroup resident at once (items are dealt out round-robin)
+  const dim3 g512(kNumCUs * kGroupedBlocksPerCU512);
+  if (L.H == 7168)
+    hipLaunchKernelGGL((kb_gateup<512, 14>), g512, dim3(kBlk), 0, s, L);
+  else if (L.H == 8192)
+    hipLaunchKernelGGL((kb_gateup<512, 16>), g512, dim3(kBlk), 0, s, L);
+  else if (L.H % 512 == 0)
+    hipLaunchKernelGGL((kb_gateup<512, 0>), g512, dim3(kBlk), 0, s, L);
+  else
+    hipLaunchKernelGGL((kb_gateup<256, 0>), dim3(kNumCUs * kGroupedBlocksPerCU), dim3(kBlk), 0, s, L);
   return hipPeekAtLastError();
 }
 
 hipError_t launch_down_tb(const LayerTB& L, hipStream_t s) {
   const dim3 grid(kNumCUs * kDownBlocksPerCU);
-  if (L.F % 256 == 0)
-    hipLaunchKernelGGL(kb_down<256>, grid, dim3(kDnBlock), 0, s, L);
+  if (L.F == 2048)
+    hipLaunchKernelGGL((kb_down<512, 4>), grid, dim3(kDnBlock), 0, s, L);
+  else if (L.F % 512 == 0)
+    hipLaunchKernelGGL((kb_down<512, 0>), grid, dim3(kDnBlock), 0, s, L);
+  else if (L.F % 256 == 0)
+    hipLaunchKernelGGL((kb_down<256, 0>), grid, dim3(kDnBlock), 0, s, L);
   else
-    hipLaunchKernelGGL(kb_down<128>, grid, dim3(kDnBlock), 0, s, L);
+    hipLaunchKernelGGL((kb_down<128, 0>), grid, dim3(kDnBlock), 0, s, L);
   return hipPeekAtLastError();
 }
 
