@@ -130,10 +130,12 @@ def cpu_baseline(w, router_hosts, toks, budget_s: float):
         if lim is not None:
             lim.unregister()
         pool.shutdown()
-    return {"value": round(spent / done * 1e6, 1), "unit": "µs per layer", "cores": cores,
+    # one token per call: per layer at batch 1, per token and layer otherwise
+    unit = "µs per layer" if w.T == 1 else "µs per token per layer"
+    return {"value": round(spent / done * 1e6, 1), "unit": unit, "cores": cores,
             "kind": "oracle",
-            "sample": f"{done} token(s) of {w.name} through one layer (weight set 0), fp64 "
-                      f"numpy oracle, {cores} worker threads, BLAS limited to 1 thread; "
+            "sample": f"{done} single token(s) of {w.name} through one layer (weight set 0), "
+                      f"fp64 numpy oracle, {cores} worker threads, BLAS limited to 1 thread; "
                       f"expert bytes generated before the clock starts"}
 
 
@@ -331,7 +333,7 @@ def main():
         log("[bench] timing the fp64 oracle on the host ...")
         cpu = cpu_baseline(w, [d.router_host for d in sets[0]],
                            [b[0] for b in toks_host[:8]], args.cpu_seconds)
-        log(f"[bench] oracle: {cpu['value']} µs/layer on {cpu['cores']} threads")
+        log(f"[bench] oracle: {cpu['value']} {cpu['unit']} on {cpu['cores']} threads")
 
     line = {
         "metric": METRIC, "value": round(us_layer, 3), "unit": "µs/layer",
