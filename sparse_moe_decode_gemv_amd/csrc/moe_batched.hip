@@ -251,10 +251,13 @@ struct GuRegs {
 };
 
 // A wave's 16-row MXFP4 weight tile: codes [16][rowc bytes] and scales
-// [16][rows bytes] from wave-uniform bases (lane r reads row r).  Codes are
-// streamed (nontemporal); a chunk needs only 16 scale bytes of each row, so
-// the scale lines are read with the default policy and stay in L2 for the
-// tile's later chunks instead of being fetched from HBM again per chunk.  Every
+// [16][rows bytes] from wave-uniform bases (lane r reads row r).  Both are
+// read with the default cache policy, not the nontemporal one: a request
+// covers 64 bytes of each row, so every 128-byte code line is completed by
+// the next request, and a chunk needs only 16 scale bytes of each row, so a
+// tile's scale lines serve all its chunks.  Nontemporal requests fetched
+// such lines from HBM again (measured: batch-64 layer 3.0 ms with both
+// nontemporal, 2.43 ms with cached scales, 2.26 ms with both cached).  Every
 // request uses a per-lane offset fixed for the whole tile plus the chunk's
 // position as a scalar offset, so no address register is rebuilt (or
 // overwritten by a load) inside the chunk loop.  A request past the last
@@ -282,7 +285,7 @@ __device__ __forceinline__ void ld_tile(uint4 (&a)[KC / 128], uint32_t (&sc)[KC 
   const uint32_t soc = cc * (KC / 2), sos = cc * (KC / 32);
 #pragma unroll
   for (int kk = 0; kk < KC / 128; ++kk) {  // block cc * KC / 32 + 4 kk + q of row r
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(voc + 64u * kk), (int)soc, kBufNT);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(voc + 64u * kk), (int)soc, 0);
     a[kk] = make_uint4(v[0], v[1], v[2], v[3]);
     sc[kk] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)(vos + 4u * kk), (int)sos, 0);
   }
