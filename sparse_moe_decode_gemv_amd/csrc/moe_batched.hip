@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
   __shared__ TokLds<KC> S;
   constexpr int PER = KC / 128;  // staged uint4 per thread per chunk
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
-  const int ng = L.ginfo[0];
+  const int ng = ld_uniform(L.ginfo);  // grouping tables: scalar loads
   const int quads = L.F / (kTileRows * kWv);
   const int nitems = ng * quads;
   const int nch = NCH ? NCH : L.H / KC;
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
   const auto rx = buf_rsrc(L.x, (uint32_t)L.T * (uint32_t)L.H * 2u);
   for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
     const int g = it / quads, rq = it - g * quads;
-    const int e = L.g_expert[g], start = L.g_start[g], m = L.g_count[g];
+    const int e = ld_uniform(L.g_expert + g), start = ld_uniform(L.g_start + g), m = ld_uniform(L.g_count + g);
     const bool sh = e >= L.E;
     const size_t row0 = (sh ? 0 : (size_t)e * L.F) + (size_t)(rq * kWv + wid) * kTileRows;
     const Tile G = make_tile(sh ? L.sg_codes : L.g_codes, sh ? L.sg_scales : L.g_scales, row0, L.H);
@@ -459,18 +459,18 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
   __shared__ TokLds<KC> Sh, Sl;
   constexpr int PER = KC / 128;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
-  const int ng = L.ginfo[0];
+  const int ng = ld_uniform(L.ginfo);  // grouping tables: scalar loads
   const int slabs = L.H / (kTileRows * kDnWaves);
   const int nitems = ng * slabs;
   const int nch = NCH ? NCH : L.F / KC;
-  const bool st_lo = tid >= 256;  // staging: threads 0..255 stage a_hi, 256..511 a_lo
+  const bool st_lo = wid >= kDnWaves / 2;  // staging: waves 0..3 stage a_hi, 4..7 a_lo
   const int sc = (tid & 255) >> 4, sj = (tid & 15) * PER;
-  // staged pairs: a_hi (threads 0..255) or a_lo (256..511), [pairs][F] bf16
+  // staged pairs: a_hi (waves 0..3) or a_lo (waves 4..7), [pairs][F] bf16
   const uint32_t npairs = (uint32_t)(L.T * L.k + L.S * L.T);
   const auto ra = buf_rsrc(st_lo ? L.act_lo : L.act_hi, npairs * (uint32_t)L.F * 2u);
   for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
     const int g = it / slabs, sb = it - g * slabs;
-    const int e = L.g_expert[g], start = L.g_start[g], m = L.g_count[g];
+    const int e = ld_uniform(L.g_expert + g), start = ld_uniform(L.g_start + g), m = ld_uniform(L.g_count + g);
     const bool sh = e >= L.E;
     const int rt = sb * kDnWaves + wid;
     const size_t row0 = (sh ? 0 : (size_t)e * L.H) + (size_t)rt * kTileRows;
@@ -529,6 +529,100 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
         *reinterpret_cast<float4*>(L.y + (size_t)(start + n0 + r) * L.H + rt * kTileRows + 4 * q) = v;
       }
     }
+  }
+}
+
+// The down kernel for an even, compile-time chunk count (FFN 2048: four
+// chunks of 512).  A wave's work is the sequence of its (item, token tile)
+// units, and it runs that sequence as one stream of chunks: the last two
+// chunks of a unit request the next unit's first two, so a unit starts with
+// its weights already in flight instead of a cold pipeline (with four
+// chunks per unit, that start was most of a unit's time).  Past the last
+// unit the requests go through empty descriptors and the output store
+// through a range check, so that no request sits under a branch.
+template <int KC, int NCH>
+__global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
+  static_assert(NCH >= 2 && NCH % 2 == 0, "units alternate register sets by chunk parity");
+  __shared__ TokLds<KC> Sh, Sl;
+  constexpr int PER = KC / 128;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
+  const int ng = ld_uniform(L.ginfo);  // grouping tables: scalar loads
+  const int slabs = L.H / (kTileRows * kDnWaves);
+  const int nitems = ng * slabs;
+  // staging: waves 0..3 stage a_hi, 4..7 a_lo (a wave-uniform choice, so the
+  // descriptor stays in scalar registers)
+  const bool st_lo = wid >= kDnWaves / 2;
+  const int sc = (tid & 255) >> 4, sj = (tid & 15) * PER;
+  const uint32_t npairs = (uint32_t)(L.T * L.k + L.S * L.T);
+  const uint16_t* abase = st_lo ? L.act_lo : L.act_hi;
+  const auto ra = buf_rsrc(abase, npairs * (uint32_t)L.F * 2u), ra0 = buf_rsrc(abase, 0u);
+  const auto ry = buf_rsrc(L.y, npairs * (uint32_t)L.H * 4u);
+  uint4 (*sbuf[2])[KC / 8 + 1] = {st_lo ? Sl.b[0] : Sh.b[0], st_lo ? Sl.b[1] : Sh.b[1]};
+
+  struct Unit {
+    Tile D;
+    uint32_t voc, vos, xvo;
+    int pair0, m, n0, rt;
+    bool live;
+  };
+  auto unit_at = [&](int it, int n0) {
+    Unit u;
+    u.live = it < nitems;
+    const int itc = u.live ? it : nitems - 1;
+    const int g = itc / slabs, sb = itc - g * slabs;
+    const int e = ld_uniform(L.g_expert + g), start = ld_uniform(L.g_start + g), m = ld_uniform(L.g_count + g);
+    const bool sh = e >= L.E;
+    u.rt = sb * kDnWaves + wid;
+    const size_t row0 = (sh ? 0 : (size_t)e * L.H) + (size_t)u.rt * kTileRows;
+    u.D = make_tile(sh ? L.sd_codes : L.d_codes, sh ? L.sd_scales : L.d_scales, row0, L.F);
+    u.voc = (uint32_t)r * u.D.rowc + 16u * (uint32_t)q;
+    u.vos = (uint32_t)r * u.D.rows + (uint32_t)q;
+    const int cs = n0 + sc < m ? n0 + sc : m - 1;
+    u.xvo = (uint32_t)(start + cs) * (uint32_t)L.F * 2u + 16u * (uint32_t)sj;
+    u.pair0 = start + n0;
+    u.m = m;
+    u.n0 = n0;
+    return u;
+  };
+  auto load_chunk = [&](const Unit& u, int c, DnRegs<KC>& A, Stage<PER>& X) {
+    X.load(u.live ? ra : ra0, u.xvo, (uint32_t)c * (uint32_t)(KC * 2));
+    __builtin_amdgcn_sched_barrier(0);
+    dn_load_a<KC>(A, u.D, u.voc, u.vos, u.live ? c : NCH, NCH);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int it = blockIdx.x;
+  if (it >= nitems) return;
+  Unit cur = unit_at(it, 0);
+  DnRegs<KC> A0, A1;
+  Stage<PER> xa, xb;
+  load_chunk(cur, 0, A0, xa);
+  load_chunk(cur, 1, A1, xb);
+  xa.store(&sbuf[0][sc][sj]);
+  __syncthreads();
+  for (;;) {
+    const bool more = cur.n0 + 16 < cur.m;
+    const Unit nxt = unit_at(more ? it : it + (int)gridDim.x, more ? cur.n0 + 16 : 0);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      DnRegs<KC>& Ac = (c & 1) ? A1 : A0;
+      Stage<PER>& xl = (c & 1) ? xb : xa;
+      const Stage<PER>& xs = (c & 1) ? xa : xb;
+      dn_mma<KC>(Ac, Sh.b[c & 1], Sl.b[c & 1], q, r, acc);
+      if (c + 2 < NCH) load_chunk(cur, c + 2, Ac, xl);
+      else load_chunk(nxt, c + 2 - NCH, Ac, xl);
+      xs.store(&sbuf[(c + 1) & 1][sc][sj]);
+      __syncthreads();
+    }
+    // rows of valid pairs only (the store's range check drops the others)
+    const bool ok = cur.n0 + r < cur.m;
+    const uint32_t yo = ok ? 4u * ((uint32_t)(cur.pair0 + r) * (uint32_t)L.H + (uint32_t)(cur.rt * kTileRows + 4 * q))
+                           : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ry, (int)yo, 0, 0);
+    if (!nxt.live) break;
+    if (!more) it += (int)gridDim.x;
+    cur = nxt;
   }
 }
 
@@ -684,7 +778,7 @@ hipError_t launch_gateup_tb(const LayerTB& L, hipStream_t s) {
 hipError_t launch_down_tb(const LayerTB& L, hipStream_t s) {
   const dim3 grid(kNumCUs * kDownBlocksPerCU);
   if (L.F == 2048)
-    hipLaunchKernelGGL((kb_down<512, 4>), grid, dim3(kDnBlock), 0, s, L);
+    hipLaunchKernelGGL((kb_down_flat<512, 4>), grid, dim3(kDnBlock), 0, s, L);
   else if (L.F % 512 == 0)
     hipLaunchKernelGGL((kb_down<512, 0>), grid, dim3(kDnBlock), 0, s, L);
   else if (L.F % 256 == 0)
