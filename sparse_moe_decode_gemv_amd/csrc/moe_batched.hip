@@ -247,7 +247,7 @@ struct TokLds {
 template <int KC>
 struct GuRegs {
   uint4 ag[KC / 128], au[KC / 128];
-  uint32_t sg[KC / 128], su[KC / 128];
+  uint32_t sg, su;  // scale dwords (see ld_tile)
 };
 
 // A wave's 16-row MXFP4 weight tile: codes [16][rowc bytes] and scales
@@ -276,9 +276,13 @@ __device__ __forceinline__ Tile make_tile(const uint8_t* codes, const uint8_t* s
   return {codes + r0 * (size_t)(K / 2), scales + r0 * (size_t)(K / 32), (uint32_t)K / 2, (uint32_t)K / 32};
 }
 
+// Scales: the chunk's KC / 32 scale bytes of row r are KC / 128 dwords;
+// lane (q, r) requests dword q of them (one request per matrix and chunk,
+// rather than one byte request per block), and the byte of block
+// 4 kk + q is later taken from lane (kk, r) with ds_bpermute (scale_of).
 template <int KC>
-__device__ __forceinline__ void ld_tile(uint4 (&a)[KC / 128], uint32_t (&sc)[KC / 128], const Tile& T,
-                                        uint32_t voc, uint32_t vos, int c, int nch) {
+__device__ __forceinline__ void ld_tile(uint4 (&a)[KC / 128], uint32_t& sd, const Tile& T, uint32_t voc,
+                                        uint32_t vos, int c, int nch) {
   const bool live = c < nch;
   const uint32_t cc = (uint32_t)(live ? c : nch - 1);
   const auto rc = buf_rsrc(T.c, live ? 16u * T.rowc : 0u), rs = buf_rsrc(T.s, live ? 16u * T.rows : 0u);
@@ -287,8 +291,21 @@ __device__ __forceinline__ void ld_tile(uint4 (&a)[KC / 128], uint32_t (&sc)[KC 
   for (int kk = 0; kk < KC / 128; ++kk) {  // block cc * KC / 32 + 4 kk + q of row r
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(voc + 64u * kk), (int)soc, 0);
     a[kk] = make_uint4(v[0], v[1], v[2], v[3]);
-    sc[kk] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)(vos + 4u * kk), (int)sos, 0);
   }
+  sd = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)vos, (int)sos, 0);
+}
+// Per-lane scale offsets of a tile: codes of block q, scale dword q (the
+// last dword for lanes past the chunk's dwords).
+template <int KC>
+__device__ __forceinline__ void tile_offsets(const Tile& T, int q, int r, uint32_t& voc, uint32_t& vos) {
+  constexpr int ND = KC / 128;
+  voc = (uint32_t)r * T.rowc + 16u * (uint32_t)q;
+  vos = (uint32_t)r * T.rows + 4u * (uint32_t)(q < ND ? q : ND - 1);
+}
+// E8M0 scale of block 4 kk + q of lane (q, r)'s row, from lane (kk, r)'s dword.
+__device__ __forceinline__ float scale_of(uint32_t sd, int kk, int q, int r) {
+  const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (16 * kk + r), (int)sd);
+  return e8m0_to_f32(byte_of(w, q));
 }
 
 // Token-activation staging: PER 16-byte pieces per thread from a row of a
@@ -321,7 +338,7 @@ __device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, const uint4 (*bt)[KC
                                        int r, f32x4& cg, f32x4& cu) {
 #pragma unroll
   for (int kk = 0; kk < KC / 128; ++kk) {
-    const float fg = e8m0_to_f32(R.sg[kk]), fu = e8m0_to_f32(R.su[kk]);
+    const float fg = scale_of(R.sg, kk, q, r), fu = scale_of(R.su, kk, q, r);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 bv = as_bf16x8(bt[r][kk * 16 + 4 * q + s]);
@@ -353,7 +370,8 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
     const size_t row0 = (sh ? 0 : (size_t)e * L.F) + (size_t)(rq * kWv + wid) * kTileRows;
     const Tile G = make_tile(sh ? L.sg_codes : L.g_codes, sh ? L.sg_scales : L.g_scales, row0, L.H);
     const Tile U = make_tile(sh ? L.su_codes : L.u_codes, sh ? L.su_scales : L.u_scales, row0, L.H);
-    const uint32_t voc = (uint32_t)r * G.rowc + 16u * (uint32_t)q, vos = (uint32_t)r * G.rows + (uint32_t)q;
+    uint32_t voc, vos;
+    tile_offsets<KC>(G, q, r, voc, vos);
     for (int n0 = 0; n0 < m; n0 += 16) {
       const int cs = n0 + sc < m ? n0 + sc : m - 1;
       const uint32_t xvo = (uint32_t)token_of(L, L.order[start + cs]) * (uint32_t)L.H * 2u + 16u * (uint32_t)sj;
@@ -430,7 +448,7 @@ constexpr int kDnBlock = kDnWaves * kWave;
 template <int KC>
 struct DnRegs {
   uint4 a[KC / 128];
-  uint32_t sc[KC / 128];
+  uint32_t sc;  // scale dword (see ld_tile)
 };
 
 template <int KC>
@@ -444,7 +462,7 @@ __device__ __forceinline__ void dn_mma(const DnRegs<KC>& R, const uint4 (*bh)[KC
                                        const uint4 (*bl)[KC / 8 + 1], int q, int r, f32x4& acc) {
 #pragma unroll
   for (int kk = 0; kk < KC / 128; ++kk) {
-    const float f = e8m0_to_f32(R.sc[kk]);
+    const float f = scale_of(R.sc, kk, q, r);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 av = fp4x8_to_bf16(dword_of(R.a[kk], s), f);
@@ -475,7 +493,8 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
     const int rt = sb * kDnWaves + wid;
     const size_t row0 = (sh ? 0 : (size_t)e * L.H) + (size_t)rt * kTileRows;
     const Tile D = make_tile(sh ? L.sd_codes : L.d_codes, sh ? L.sd_scales : L.d_scales, row0, L.F);
-    const uint32_t voc = (uint32_t)r * D.rowc + 16u * (uint32_t)q, vos = (uint32_t)r * D.rows + (uint32_t)q;
+    uint32_t voc, vos;
+    tile_offsets<KC>(D, q, r, voc, vos);
     for (int n0 = 0; n0 < m; n0 += 16) {
       const int cs = n0 + sc < m ? n0 + sc : m - 1;
       const uint32_t xvo = (uint32_t)(start + cs) * (uint32_t)L.F * 2u + 16u * (uint32_t)sj;
@@ -575,8 +594,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
     u.rt = sb * kDnWaves + wid;
     const size_t row0 = (sh ? 0 : (size_t)e * L.H) + (size_t)u.rt * kTileRows;
     u.D = make_tile(sh ? L.sd_codes : L.d_codes, sh ? L.sd_scales : L.d_scales, row0, L.F);
-    u.voc = (uint32_t)r * u.D.rowc + 16u * (uint32_t)q;
-    u.vos = (uint32_t)r * u.D.rows + (uint32_t)q;
+    tile_offsets<KC>(u.D, q, r, u.voc, u.vos);
     const int cs = n0 + sc < m ? n0 + sc : m - 1;
     u.xvo = (uint32_t)(start + cs) * (uint32_t)L.F * 2u + 16u * (uint32_t)sj;
     u.pair0 = start + n0;
