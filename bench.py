@@ -147,7 +147,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="k3_batch1",
                     choices=["tiny", "k3_batch1", "k3_tp16_slice", "k3_stack8",
-                             "k3_batch64_zipf"])
+                             "k3_batch64_zipf", "k3_verify8"])
     ap.add_argument("--sets", type=int, default=4, help="resident weight sets rotated")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly (no graph), e.g. under counter profiling")

@@ -52,7 +52,7 @@ TENSOR = {
     "down_codes": 5, "down_scales": 6,
     "s_gate_codes": 7, "s_gate_scales": 8, "s_up_codes": 9, "s_up_scales": 10,
     "s_down_codes": 11, "s_down_scales": 12,
-    "router": 20, "token": 21, "gamma": 22, "zipf_perm": 23,
+    "router": 20, "token": 21, "gamma": 22, "zipf_perm": 23, "token_base": 24,
 }
 
 
@@ -71,6 +71,7 @@ class Workload:
     L: int = 1
     eps: float = 1e-6
     zipf_s: float | None = None
+    corr: float | None = None  # tokens of one sequence share this fraction of variance
     seed: int = 0
     notes: str = field(default="", compare=False)
 
@@ -92,6 +93,9 @@ WORKLOADS = {
                                 seed=0x5EED0003),
     "k3_stack8": Workload("k3_stack8", T=1, H=7168, E=896, k=16, F=2048, S=1,
                           Fs=2048, L=8, seed=0x5EED0004),
+    # speculative-decode verify shape: one sequence's token and 7 drafts
+    "k3_verify8": Workload("k3_verify8", T=8, H=7168, E=896, k=16, F=2048, S=1,
+                           Fs=2048, corr=0.5, seed=0x5EED0005),
 }
 
 
@@ -167,8 +171,18 @@ def uniform_bf16(seed, layer, tensor, shape, lo, hi, draw=0) -> np.ndarray:
 
 
 def token(w: Workload, draw: int) -> np.ndarray:
-    """One activation row bf16[H] ~ N(0, 1); ``draw`` selects the sample."""
-    return normal_bf16(w.seed, 0, "token", (w.H,), 1.0, draw)
+    """One activation row bf16[H] ~ N(0, 1); ``draw`` selects the sample.
+
+    With ``w.corr`` = rho the draws come in sequences of T consecutive
+    draws (draw // T) that share a component: x = sqrt(rho) b + sqrt(1 - rho) z
+    with b ~ N(0, 1) per sequence and z ~ N(0, 1) per draw, so tokens of one
+    sequence have correlation rho and overlapping routing (the verify step of
+    speculative decoding runs one sequence's token and its drafts together)."""
+    if w.corr is None:
+        return normal_bf16(w.seed, 0, "token", (w.H,), 1.0, draw)
+    z = _rng(w.seed, 0, "token", draw).standard_normal(w.H)
+    b = _rng(w.seed, 0, "token_base", draw // w.T).standard_normal(w.H)
+    return bf16_from_f64(np.sqrt(w.corr) * b + np.sqrt(1.0 - w.corr) * z)
 
 
 def zipf_row_scales(E: int, k: int, s: float, seed: int, p_max: float = 0.45):

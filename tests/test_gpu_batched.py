@@ -116,6 +116,17 @@ def test_k3_batch64_zipf_layer():
     assert check_topk(idx, {"logits": Lr, "idx": O.topk_select(Lr, w.k)}, w.k) == 64
 
 
+def test_k3_verify8_layer():
+    """The speculative-decode verify shape: one sequence's token and seven
+    drafts (correlated activations, overlapping routing) through the
+    K3-shaped layer; every token against the oracle."""
+    w = G.WORKLOADS["k3_verify8"]
+    X, out, idx = batched_parity(w, 8)
+    n = len(np.unique(idx))
+    print(f"distinct experts {n} of {8 * w.k} slots")
+    assert n < 8 * w.k  # the drafts share experts
+
+
 def test_batch_matches_single_token_calls():
     """Token t of a T = 64 call agrees with a T = 1 call on the same token:
     same experts, outputs within the layer tolerance of each other."""

@@ -67,3 +67,16 @@ def test_zipf_scales_skew_loads():
     a = G.zipf_row_scales(896, 16, 1.1, 3)
     assert a.shape == (896,) and np.all(a > 0)
     assert a.max() / np.median(a) > 3
+
+
+def test_verify_tokens_are_correlated_within_a_sequence():
+    """k3_verify8 draws: tokens of one sequence (draw // T) have correlation
+    close to the workload's rho, tokens of different sequences close to 0."""
+    w = G.WORKLOADS["k3_verify8"]
+    xs = np.stack([(G.token(w, d).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                   for d in range(2 * w.T)])
+    c = np.corrcoef(xs)
+    same = [c[i, j] for i in range(w.T) for j in range(w.T) if i < j]
+    cross = [c[i, j] for i in range(w.T) for j in range(w.T, 2 * w.T)]
+    assert abs(np.mean(same) - w.corr) < 0.03, np.mean(same)
+    assert abs(np.mean(cross)) < 0.03, np.mean(cross)
