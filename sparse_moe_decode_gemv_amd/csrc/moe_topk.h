@@ -136,16 +136,22 @@ __device__ inline void topk_softmax_block(const float (&lg)[kTopkPerThread], int
         rank += (kj > mk || (kj == mk && ij < mi)) ? 1 : 0;
       }
     }
-    const uint32_t top = wave_max_u32(mk);
-    const float l = f32_from_order_key(mk);
-    const float ex = act ? expf(l - f32_from_order_key(top)) : 0.f;
+    // The gather's atomic slots put the selected experts in the lanes in
+    // whatever order the atomics ran; move each to the lane of its rank
+    // first, so that the softmax sum adds in a fixed order (identical
+    // weights on every call).
+    const int dst = act ? rank : lane;
+    const uint32_t rk = (uint32_t)__builtin_amdgcn_ds_permute(4 * dst, (int)mk);
+    const int ri = __builtin_amdgcn_ds_permute(4 * dst, mi);
+    const uint32_t top = (uint32_t)__builtin_amdgcn_readlane((int)rk, 0);
+    const float ex = act ? expf(f32_from_order_key(rk) - f32_from_order_key(top)) : 0.f;
     const float sum = wave_sum(ex);
     if (act) {
       const float w = ex / sum;
-      idx[rank] = mi;
-      wts[rank] = w;
-      if (idx_out) idx_out[rank] = mi;
-      if (w_out) w_out[rank] = w;
+      idx[lane] = ri;
+      wts[lane] = w;
+      if (idx_out) idx_out[lane] = ri;
+      if (w_out) w_out[lane] = w;
     }
   }
 }

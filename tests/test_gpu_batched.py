@@ -150,9 +150,14 @@ def test_batch_matches_single_token_calls():
     release_device_layers()
 
 
-def test_batched_graph_replay_matches_eager():
+@pytest.mark.parametrize("name", ["ragged_shared", "k3_verify8"])
+def test_batched_graph_replay_matches_eager(name):
+    """A batched layer captured in a HIP graph and replayed with new inputs
+    copied in between equals the eager call bit for bit, every replay.  At
+    the K3 shape this covers the unrolled gate/up and the unit-stream down
+    kernels; the small shape the generic loops."""
     t = torch()
-    w = SMALL["ragged_shared"]
+    w = SMALL[name] if name in SMALL else G.WORKLOADS[name]
     dl = device_layer(w, 0)
     T = 8
     batches = [tokens_of(w, dl, T, start=1000 + 50 * i) for i in range(3)]
@@ -181,6 +186,7 @@ def test_batched_graph_replay_matches_eager():
             g.replay()
             t.cuda.synchronize()
             assert np.array_equal(host_u16(out), eager[i]), (rep, i)
+    release_device_layers()
 
 
 def test_batched_stack_teacher_forced():
