@@ -27,6 +27,8 @@ SMALL = {
     "k1_f128": G.Workload("k1_f128", T=1, H=512, E=16, k=1, F=128, S=1, Fs=128, seed=0x5EED0203),
     # the largest hidden size: the gate/up chunk loop unrolled for 16 chunks
     "h8192": G.Workload("h8192_b", T=1, H=8192, E=16, k=2, F=256, S=1, Fs=256, seed=0x5EED0204),
+    # the most experts and the largest top-k the library accepts together
+    "emax": G.Workload("emax_b", T=1, H=512, E=1024, k=32, F=128, S=1, Fs=128, seed=0x5EED0205),
 }
 
 

@@ -27,6 +27,8 @@ SMALL = {
     "f640": G.Workload("f640", T=1, H=768, E=10, k=2, F=640, S=0, Fs=0, seed=0x5EED0109),
     "f1536": G.Workload("f1536", T=1, H=1024, E=8, k=2, F=1536, S=1, Fs=1536, seed=0x5EED010A),
     "f8192": G.Workload("f8192", T=1, H=256, E=4, k=2, F=8192, S=1, Fs=8192, seed=0x5EED010B),
+    # the most experts and the largest top-k the library accepts together
+    "emax": G.Workload("emax", T=1, H=512, E=1024, k=32, F=128, S=1, Fs=128, seed=0x5EED010C),
 }
 
 
