@@ -472,7 +472,9 @@ __device__ __forceinline__ void dn_mma(const DnRegs<KC>& R, const uint4 (*bh)[KC
   }
 }
 
-template <int KC, int NCH>
+// The general down kernel (any FFN width that is a multiple of KC; FFN 2048
+// runs kb_down_flat below).
+template <int KC>
 __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
   __shared__ TokLds<KC> Sh, Sl;
   constexpr int PER = KC / 128;
@@ -480,7 +482,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
   const int ng = ld_uniform(L.ginfo);  // grouping tables: scalar loads
   const int slabs = L.H / (kTileRows * kDnWaves);
   const int nitems = ng * slabs;
-  const int nch = NCH ? NCH : L.F / KC;
+  const int nch = L.F / KC;
   const bool st_lo = wid >= kDnWaves / 2;  // staging: waves 0..3 stage a_hi, 4..7 a_lo
   const int sc = (tid & 255) >> 4, sj = (tid & 15) * PER;
   // staged pairs: a_hi (waves 0..3) or a_lo (waves 4..7), [pairs][F] bf16
@@ -517,27 +519,17 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
       auto step = [&](int c, DnRegs<KC>& Ac, Stage<PER>& xl, const Stage<PER>& xs, int bu,
                       uint4 (*bs)[KC / 8 + 1]) {
         dn_mma<KC>(Ac, Sh.b[bu], Sl.b[bu], q, r, acc);
-        if (!NCH || c + 2 < nch) {
-          xl.load(ra, xvo, xso(c + 2));
-          __builtin_amdgcn_sched_barrier(0);
-          dn_load_a<KC>(Ac, D, voc, vos, c + 2, nch);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (!NCH || c + 1 < nch) xs.store(&bs[sc][sj]);
+        xl.load(ra, xvo, xso(c + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        dn_load_a<KC>(Ac, D, voc, vos, c + 2, nch);
+        __builtin_amdgcn_sched_barrier(0);
+        xs.store(&bs[sc][sj]);
         __syncthreads();
       };
-      if constexpr (NCH > 0) {
-#pragma unroll
-        for (int c = 0; c < NCH; c += 2) {
-          step(c, A0, xa, xb, 0, sbuf1);
-          if (c + 1 < NCH) step(c + 1, A1, xb, xa, 1, sbuf0);
-        }
-      } else {
-        for (int c = 0; c < nch; c += 2) {
-          step(c, A0, xa, xb, 0, sbuf1);
-          if (c + 1 >= nch) break;
-          step(c + 1, A1, xb, xa, 1, sbuf0);
-        }
+      for (int c = 0; c < nch; c += 2) {
+        step(c, A0, xa, xb, 0, sbuf1);
+        if (c + 1 >= nch) break;
+        step(c + 1, A1, xb, xa, 1, sbuf0);
       }
       if (n0 + r < m) {
         float4 v;
@@ -798,11 +790,11 @@ hipError_t launch_down_tb(const LayerTB& L, hipStream_t s) {
   if (L.F == 2048)
     hipLaunchKernelGGL((kb_down_flat<512, 4>), grid, dim3(kDnBlock), 0, s, L);
   else if (L.F % 512 == 0)
-    hipLaunchKernelGGL((kb_down<512, 0>), grid, dim3(kDnBlock), 0, s, L);
+    hipLaunchKernelGGL(kb_down<512>, grid, dim3(kDnBlock), 0, s, L);
   else if (L.F % 256 == 0)
-    hipLaunchKernelGGL((kb_down<256, 0>), grid, dim3(kDnBlock), 0, s, L);
+    hipLaunchKernelGGL(kb_down<256>, grid, dim3(kDnBlock), 0, s, L);
   else
-    hipLaunchKernelGGL((kb_down<128, 0>), grid, dim3(kDnBlock), 0, s, L);
+    hipLaunchKernelGGL(kb_down<128>, grid, dim3(kDnBlock), 0, s, L);
   return hipPeekAtLastError();
 }
 
