@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
   const int nitems = ng * quads;
   const int nch = NCH ? NCH : L.H / KC;
   const int sc = tid >> 4, sj = (tid & 15) * PER;  // staging: token row, first uint4
-  const auto rx = buf_rsrc(L.x, (uint32_t)L.T * (uint32_t)L.H * 2u);
+  const auto rx = buf_rsrc(L.x, (uint32_t)L.T * (uint32_t)L.H * 2u), rx0 = buf_rsrc(L.x, 0u);
   for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
     const int g = it / quads, rq = it - g * quads;
     const int e = ld_uniform(L.g_expert + g), start = ld_uniform(L.g_start + g), m = ld_uniform(L.g_count + g);
@@ -376,14 +376,17 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
       const int cs = n0 + sc < m ? n0 + sc : m - 1;
       const uint32_t xvo = (uint32_t)token_of(L, L.order[start + cs]) * (uint32_t)L.H * 2u + 16u * (uint32_t)sj;
       auto xso = [&](int c) { return (uint32_t)(c < nch ? c : nch - 1) * (uint32_t)(KC * 2); };
+      // this wave stages rows 4 wid .. 4 wid + 3; past the group's tokens it
+      // requests nothing (empty descriptor: zeros, whose products are dropped)
+      const auto rxw = 4 * wid < m - n0 ? rx : rx0;
       f32x4 cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
       GuRegs<KC> A0, A1;
       Stage<PER> xa, xb;
-      xa.load(rx, xvo, xso(0));
+      xa.load(rxw, xvo, xso(0));
       __builtin_amdgcn_sched_barrier(0);
       gu_load_a<KC>(A0, G, U, voc, vos, 0, nch);
       __builtin_amdgcn_sched_barrier(0);
-      xb.load(rx, xvo, xso(1));
+      xb.load(rxw, xvo, xso(1));
       __builtin_amdgcn_sched_barrier(0);
       gu_load_a<KC>(A1, G, U, voc, vos, 1, nch);
       __builtin_amdgcn_sched_barrier(0);
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
                       const uint4 (*bu)[KC / 8 + 1], uint4 (*bs)[KC / 8 + 1]) {
         gu_mma<KC>(Ac, bu, q, r, cg, cu);
         if (!NCH || c + 2 < nch) {
-          xl.load(rx, xvo, xso(c + 2));
+          xl.load(rxw, xvo, xso(c + 2));
           __builtin_amdgcn_sched_barrier(0);
           gu_load_a<KC>(Ac, G, U, voc, vos, c + 2, nch);
           __builtin_amdgcn_sched_barrier(0);
@@ -594,8 +597,11 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
     u.n0 = n0;
     return u;
   };
+  // a wave stages rows 4 (wid & 3) .. + 3 of the unit's 16; when they are all
+  // past the unit's pairs it requests nothing (empty descriptor: zeros)
+  const int srow0 = 4 * (wid & 3);
   auto load_chunk = [&](const Unit& u, int c, DnRegs<KC>& A, Stage<PER>& X) {
-    X.load(u.live ? ra : ra0, u.xvo, (uint32_t)c * (uint32_t)(KC * 2));
+    X.load(u.live && srow0 < u.m - u.n0 ? ra : ra0, u.xvo, (uint32_t)c * (uint32_t)(KC * 2));
     __builtin_amdgcn_sched_barrier(0);
     dn_load_a<KC>(A, u.D, u.voc, u.vos, u.live ? c : NCH, NCH);
     __builtin_amdgcn_sched_barrier(0);
