@@ -308,21 +308,23 @@ __device__ __forceinline__ float scale_of(uint32_t sd, int kk, int q, int r) {
   return e8m0_to_f32(byte_of(w, q));
 }
 
-// Token-activation staging: PER 16-byte pieces per thread from a row of a
-// bf16 array (one descriptor over the whole array, the row and piece as a
-// fixed per-thread offset, the chunk as a scalar offset).
+// Token-activation staging: a chunk of a token row (PER x 16 16-byte pieces)
+// is staged by 16 threads, thread j taking pieces j, j + 16, ..., so that
+// each request covers 256 contiguous bytes of the row (one descriptor over
+// the whole array, the row and piece as a fixed per-thread offset, the
+// chunk as a scalar offset).
 template <int PER>
 struct Stage {
   u32x4 v[PER];
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 16u * i), (int)soff, 0));
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 256u * i), (int)soff, 0));
   }
-  __device__ __forceinline__ void store(uint4* dst) const {
+  __device__ __forceinline__ void store(uint4* dst) const {  // dst: the thread's first piece
     u32x4* p = reinterpret_cast<u32x4*>(dst);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) p[i] = v[i];
+    for (int i = 0; i < PER; ++i) p[16 * i] = v[i];
   }
 };
 
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
   const int quads = L.F / (kTileRows * kWv);
   const int nitems = ng * quads;
   const int nch = NCH ? NCH : L.H / KC;
-  const int sc = tid >> 4, sj = (tid & 15) * PER;  // staging: token row, first uint4
+  const int sc = tid >> 4, sj = tid & 15;  // staging: token row, first piece (stride 16)
   const auto rx = buf_rsrc(L.x, (uint32_t)L.T * (uint32_t)L.H * 2u), rx0 = buf_rsrc(L.x, 0u);
   for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
     const int g = it / quads, rq = it - g * quads;
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
   const int nitems = ng * slabs;
   const int nch = L.F / KC;
   const bool st_lo = wid >= kDnWaves / 2;  // staging: waves 0..3 stage a_hi, 4..7 a_lo
-  const int sc = (tid & 255) >> 4, sj = (tid & 15) * PER;
+  const int sc = (tid & 255) >> 4, sj = tid & 15;  // token row, first piece (stride 16)
   // staged pairs: a_hi (waves 0..3) or a_lo (waves 4..7), [pairs][F] bf16
   const uint32_t npairs = (uint32_t)(L.T * L.k + L.S * L.T);
   const auto ra = buf_rsrc(st_lo ? L.act_lo : L.act_hi, npairs * (uint32_t)L.F * 2u);
@@ -566,7 +568,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
   // staging: waves 0..3 stage a_hi, 4..7 a_lo (a wave-uniform choice, so the
   // descriptor stays in scalar registers)
   const bool st_lo = wid >= kDnWaves / 2;
-  const int sc = (tid & 255) >> 4, sj = (tid & 15) * PER;
+  const int sc = (tid & 255) >> 4, sj = tid & 15;  // token row, first piece (stride 16)
   const uint32_t npairs = (uint32_t)(L.T * L.k + L.S * L.T);
   const uint16_t* abase = st_lo ? L.act_lo : L.act_hi;
   const auto ra = buf_rsrc(abase, npairs * (uint32_t)L.F * 2u), ra0 = buf_rsrc(abase, 0u);
