@@ -39,6 +39,9 @@
  *    zero.  The rest is scratch that each call writes before it reads it, so
  *    one workspace serves any number of calls on one stream.  Calls that
  *    overlap in time (different streams) need different workspaces.
+ *  - Results depend on the inputs only: a call repeated on the same inputs
+ *    (eager or replayed from a graph) gives identical bits.  Sums run in a
+ *    fixed order and no floating-point atomics are used.
  *  - Expert indices read from device memory (topk_idx arguments, or the
  *    router's own output) are clamped to [0, E) before addressing weights;
  *    an out-of-range index gives unspecified values for that slot, never an

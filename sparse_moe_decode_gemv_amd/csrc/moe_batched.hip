@@ -17,7 +17,9 @@
 //           a_hi = bf16(a) and a_lo = bf16(a - a_hi), so that the down GEMM
 //           keeps ~16 significant bits of a on bf16 MFMA.
 //  down     grouped GEMM per (group, 16-row tile of the hidden size) over
-//           a_hi and a_lo -> fp32 expert outputs per sorted pair.
+//           a_hi and a_lo -> fp32 expert outputs per sorted pair; at FFN
+//           2048 each wave runs its units as one chunk stream
+//           (kb_down_flat).
 //  combine  per token: residual + sum_j w_j y_j (slot order) + y_shared ->
 //           bf16; fixed order, no floating-point atomics.
 //
@@ -28,7 +30,11 @@
 // section "四步改造"; the pages' fast path stops at 64 tokens: page "AI手搓
 // 1.2万行代码榨干GB300!…", section 03).  Weight bytes still dominate, so the
 // grouped kernels keep consecutive waves on consecutive row tiles of one
-// expert and stream the weights with nontemporal 16-byte loads.
+// expert, request each chunk two chunks ahead with 16-byte buffer loads
+// through L2 (a request covers 64 bytes of a row, and the rest of the line
+// and the tile's scale lines are used by the next requests), and keep the
+// count of requests per chunk low (one scale dword per lane, no staging
+// requests for token rows past the group).
 //
 // MFMA v_mfma_f32_16x16x32_bf16 fragments (lane l = 16 q + r): A holds
 // A[r][8q .. 8q+7], B holds B[8q .. 8q+7][r], the result C[4q .. 4q+3][r].
