@@ -1,0 +1,37 @@
+"""The rocprofv3 summary helpers (CPU): per-kernel classification and the
+per-layer span / idle-time summary, on hand-made launch sequences."""
+from sparse_moe_decode_gemv_amd import profiling as P
+
+
+def test_gateup_launches_are_classed_by_predecessor():
+    seq = ["k1_router", "k2_gateup", "k3_slab", "k2_gateup", "k1_topk", "k2_gateup"]
+    keys = P._classify(seq)
+    assert keys[1] == "k2_gateup (in layer)"
+    assert keys[3] == "k2_gateup (stand-alone)"
+    assert keys[5] == "k2_gateup (stand-alone)"
+
+
+def test_layer_spans_of_two_batch1_layers():
+    names = ["k1_router", "k2_gateup", "k3_slab"] * 2
+    # (name, start ns, end ns): 100 ns idle inside layer 1, 500 ns between layers
+    rows = [("", 0, 4000), ("", 4100, 50000), ("", 50000, 80000),
+            ("", 80500, 84000), ("", 84000, 130000), ("", 130000, 160000)]
+    out = P.layer_spans(names, rows)
+    assert "decode layers in the trace: 2; kernels per layer: 3 (2 layers)" in out
+    assert "mean 79.75" in out          # spans 80.0 and 79.5 us
+    assert "idle between a layer's kernels us: mean 0.05" in out
+    assert "gap to the next layer us: mean 0.50" in out
+
+
+def test_layer_spans_batched_layer_with_rmsnorm_and_foreign_kernel():
+    names = ["kb_rmsnorm", "kb_router", "kb_topk", "kb_group", "kb_gateup", "kb_down_flat",
+             "kb_combine", "copyBuffer", "kb_router", "kb_topk"]
+    rows = [("", 1000 * i, 1000 * i + 900) for i in range(len(names))]
+    out = P.layer_spans(names, rows)
+    # one complete 7-kernel layer; the trailing partial layer is not counted
+    assert "decode layers in the trace: 1; kernels per layer: 7 (1 layers)" in out
+    assert "kb_rmsnorm > kb_router > kb_topk > kb_group > kb_gateup > kb_down_flat > kb_combine" in out
+
+
+def test_no_layer_in_trace():
+    assert P.layer_spans(["copyBuffer"], [("", 0, 10)]) == "no complete decode layer in the trace"
