@@ -152,9 +152,26 @@ __global__ __launch_bounds__(kTopkBlock) void kb_topk(LayerTB L) {
     const int e = threadIdx.x * kTopkPerThread + i;
     if (L.logits_out && e < L.E) L.logits_out[(size_t)t * L.E + e] = s;
   }
-  const size_t o = (size_t)t * L.k;
-  topk_softmax_block(lg, L.E, L.k, tk, L.idx + o, L.wts + o, L.idx_out ? L.idx_out + o : nullptr,
-                     L.w_out ? L.w_out + o : nullptr);
+  // the selection by one wave (as for a single token): logits through LDS,
+  // lane l taking experts 16 l .. 16 l + 15; no barrier inside
+  __shared__ float lg_lds[kMaxExperts];
+#pragma unroll
+  for (int i = 0; i < kTopkPerThread; ++i) lg_lds[threadIdx.x * kTopkPerThread + i] = lg[i];
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    uint32_t key[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int e = 16 * lane + m;
+      key[m] = e < L.E ? f32_order_key(lg_lds[e]) : 0u;
+    }
+    const size_t o = (size_t)t * L.k;
+    int32_t* io = L.idx_out ? L.idx_out + o : nullptr;
+    float* wo = L.w_out ? L.w_out + o : nullptr;
+    if (!topk_softmax_wave(key, L.E, L.k, tk, L.idx + o, L.wts + o, io, wo))
+      topk_softmax_wave_rounds(key, L.E, L.k, L.idx + o, L.wts + o, io, wo);  // many ties
+  }
 }
 
 // ---------------------------------------------------------------- group
@@ -663,15 +680,39 @@ __global__ __launch_bounds__(kBlk) void kb_combine(LayerTB L) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < L.k; ++j) {
-    const float w = L.wts[(size_t)t * L.k + j];
-    int pos = L.pos_of[(size_t)t * L.k + j];
+  // The token's weights and pair positions are workgroup-uniform (scalar
+  // loads).  Whole batches of kCombineBatch slots request their rows
+  // together, then add them in slot order; the remaining slots (k not a
+  // multiple of the batch) go one at a time.  Same order of additions either
+  // way.
+  constexpr int kCombineBatch = 8;
+  const float* wt = L.wts + (size_t)t * L.k;
+  const int32_t* pt = L.pos_of + (size_t)t * L.k;
+  auto row_of = [&](int j) {
+    int pos = ld_uniform(pt + j);
     pos = pos < 0 ? 0 : (pos >= npos ? npos - 1 : pos);
-    const float4* yp = reinterpret_cast<const float4*>(L.y + (size_t)pos * L.H + h0);
-    const float4 a = yp[0], b = yp[1];
+    return reinterpret_cast<const float4*>(L.y + (size_t)pos * L.H + h0);
+  };
+  auto add = [&](float w, const float4& a, const float4& b) {
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(w, v[i], acc[i]);
+  };
+  int j0 = 0;
+  for (; j0 + kCombineBatch <= L.k; j0 += kCombineBatch) {
+    float4 ya[kCombineBatch], yb[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const float4* yp = row_of(j0 + u);
+      ya[u] = yp[0];
+      yb[u] = yp[1];
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) add(ld_uniform(wt + j0 + u), ya[u], yb[u]);
+  }
+  for (int j = j0; j < L.k; ++j) {
+    const float4* yp = row_of(j);
+    add(ld_uniform(wt + j), yp[0], yp[1]);
   }
   if (L.S) {
     const float4* yp = reinterpret_cast<const float4*>(L.y + (size_t)(P + t) * L.H + h0);

@@ -1,5 +1,5 @@
-// Top-k + softmax of one token's router logits by one 256-thread workgroup
-// (shared by the single-token and the batched paths).
+// Top-k + softmax of one token's router logits by one wave, without
+// barriers (shared by the single-token and the batched paths).
 #pragma once
 
 #include "moe_device.h"
@@ -7,154 +7,16 @@
 
 namespace moe {
 
-// Top-k + softmax by one workgroup (E <= 1024, k <= 32).  Logits become
-// order-preserving 32-bit keys (-0 folded onto +0; a larger key is a larger
-// logit); thread t of the 256 holds experts 4t .. 4t+3 (lg[], already
-// loaded by the caller).
-//  1. Radix select, most significant byte first: four passes of a 256-bin
-//     LDS histogram over the keys that still match the chosen prefix, each
-//     followed by a wave scan from the top bin down, give the exact k-th
-//     largest key T and how many keys equal to T are needed (kr).  Each
-//     wave counts into a histogram of its own (logits share their leading
-//     bytes, so a shared histogram serialises most increments on a few
-//     bins); the scan adds the four.
-//  2. Keys above T, and the kr lowest-indexed keys equal to T, are gathered.
-//  3. One wave ranks the k gathered (key, index) pairs by (key desc, index
-//     asc), each lane holding one and reading the others from their lanes,
-//     and writes them in that order with their softmax weights.
+// Batched top-k workgroups are kTopkBlock threads; thread t holds the logits
+// of experts kTopkPerThread t .. kTopkPerThread t + kTopkPerThread - 1 while
+// it sums the router's partial results.
 constexpr int kTopkBlock = 256;
 constexpr int kTopkPerThread = kMaxExperts / kTopkBlock;  // keys per thread
 
 struct TopkLds {
   alignas(16) uint32_t lmax[kWave];  // wave top-k: lane maxima
   uint64_t cand[2 * kWave];          // candidates; the upper half takes discarded stores
-  uint32_t hist[kTopkBlock / kWave][256];  // one histogram per wave
-  uint32_t sel_key[kMaxTopK];
-  int32_t sel_idx[kMaxTopK];
-  uint32_t wave_eq[kTopkBlock / kWave];
-  int32_t pick[2];  // bin found by the current pass, count above it
-  int32_t nsel;
 };
-
-__device__ inline void topk_softmax_block(const float (&lg)[kTopkPerThread], int E, int k,
-                                          TopkLds& S, int32_t* idx, float* wts,
-                                          int32_t* idx_out, float* w_out) {
-  constexpr int KPT = kTopkPerThread;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  uint32_t key[KPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) key[i] = tid * KPT + i < E ? f32_order_key(lg[i]) : 0u;
-
-  uint32_t prefix = 0u;
-  int kr = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t decided = ~(0xFFFFFFFFu >> (8 * pass));  // bytes chosen so far
-#pragma unroll
-    for (int w = 0; w < kTopkBlock / kWave; ++w) S.hist[w][tid] = 0u;
-    if (tid == 0) S.nsel = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const bool match = ((key[i] ^ prefix) & decided) == 0u;
-      if (match && key[i] != 0u) atomicAdd(&S.hist[wid][(key[i] >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wid == 0) {
-      // lane l holds bins 255-4l .. 252-4l (descending), summed over waves
-      uint32_t cnt[4], tot = 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t c = 0u;
-#pragma unroll
-        for (int w = 0; w < kTopkBlock / kWave; ++w) c += S.hist[w][255 - 4 * lane - j];
-        cnt[j] = c;
-        tot += c;
-      }
-      const uint32_t incl = wave_incl_scan_u32(tot);
-      const uint64_t over = __ballot(incl >= (uint32_t)kr);
-      const int fl = (int)__builtin_ctzll(over);
-      if (lane == fl) {
-        uint32_t cum = incl - tot;
-        int bin = 0;
-        uint32_t above = 0u;
-        bool done = false;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (!done && cum + cnt[j] >= (uint32_t)kr) {
-            bin = 255 - 4 * lane - j;
-            above = cum;
-            done = true;
-          }
-          cum += cnt[j];
-        }
-        S.pick[0] = bin;
-        S.pick[1] = (int)above;
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)S.pick[0] << shift;
-    kr -= S.pick[1];
-    __syncthreads();  // pick[] and hist[] are rewritten by the next pass
-  }
-
-  // gather: keys above T, then the kr lowest-indexed keys equal to T
-  uint32_t neq = 0u;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) neq += key[i] == prefix ? 1u : 0u;
-  const uint32_t inc = wave_incl_scan_u32(neq);
-  if (lane == kWave - 1) S.wave_eq[wid] = inc;
-  __syncthreads();
-  uint32_t before = inc - neq;
-  for (int w = 0; w < wid; ++w) before += S.wave_eq[w];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    bool take = key[i] > prefix;
-    if (key[i] == prefix) {
-      take = before < (uint32_t)kr;
-      ++before;
-    }
-    if (take) {
-      const int pos = atomicAdd(&S.nsel, 1);
-      S.sel_key[pos] = key[i];
-      S.sel_idx[pos] = tid * KPT + i;
-    }
-  }
-  __syncthreads();
-  if (wid == 0) {
-    const bool act = lane < k;
-    const uint32_t mk = act ? S.sel_key[lane] : 0u;
-    const int mi = act ? S.sel_idx[lane] : 0;
-    // rank against every candidate, read from its lane (no LDS round trips)
-    int rank = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k) {
-        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
-        const int ij = __builtin_amdgcn_readlane(mi, j);
-        rank += (kj > mk || (kj == mk && ij < mi)) ? 1 : 0;
-      }
-    }
-    // The gather's atomic slots put the selected experts in the lanes in
-    // whatever order the atomics ran; move each to the lane of its rank
-    // first, so that the softmax sum adds in a fixed order (identical
-    // weights on every call).
-    const int dst = act ? rank : lane;
-    const uint32_t rk = (uint32_t)__builtin_amdgcn_ds_permute(4 * dst, (int)mk);
-    const int ri = __builtin_amdgcn_ds_permute(4 * dst, mi);
-    const uint32_t top = (uint32_t)__builtin_amdgcn_readlane((int)rk, 0);
-    const float ex = act ? expf(f32_from_order_key(rk) - f32_from_order_key(top)) : 0.f;
-    const float sum = wave_sum(ex);
-    if (act) {
-      const float w = ex / sum;
-      idx[lane] = ri;
-      wts[lane] = w;
-      if (idx_out) idx_out[lane] = ri;
-      if (w_out) w_out[lane] = w;
-    }
-  }
-}
 
 // Sum over the 64 lanes by DPP within rows, then the four row sums (the same
 // order in every wave, so every workgroup gets the same weights).
@@ -172,8 +34,8 @@ __device__ __forceinline__ float wave_sum_rows(float v) {
 
 // Top-k + softmax by ONE wave, without barriers (E <= 1024, k <= 32).  Lane l
 // holds experts 16 l .. 16 l + 15 as order-preserving keys (key[m], 0 for an
-// absent expert); the order is the block version's: larger logit first,
-// lower index first among equal logits.  Every step is a few independent
+// absent expert); the selection orders experts by larger logit first, then
+// lower index among equal logits.  Every step is a few independent
 // compares per lane (LDS broadcast reads), not a chain of cross-lane reads.
 //  1. T = the k-th largest of the 64 lane maxima: a lane's maximum is T when
 //     at least k lane maxima are >= it and it is the largest such.  At least
