@@ -271,14 +271,16 @@ def test_deterministic_and_poison_proof():
     release_device_layers()
 
 
-M_COUNTER = 256
+M_COUNTER = 256  # MOE_WS_COUNTER_BYTES
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("name", ["tiny", "k3_batch1"])
+def test_graph_replay_matches_eager(name):
     """One layer captured in a HIP graph, replayed with new inputs copied in
-    between; every replay equals the eager call on the same input."""
+    between; every replay equals the eager call on the same input, and the
+    workspace's counter head is left at zero."""
     t = torch()
-    w = G.WORKLOADS["tiny"]
+    w = G.WORKLOADS[name]
     dl = device_layer(w, 0)
     toks = [x for _, x in pick_tokens(w, dl.router_host, 4, start=200)]
     ws = workspace(w, 1)
@@ -306,3 +308,4 @@ def test_graph_replay_matches_eager():
             g.replay()
             t.cuda.synchronize()
             assert np.array_equal(host_u16(out), eager[i]), (rep, i)
+    assert not ws[:M_COUNTER].any().item(), "counters not left at zero"
