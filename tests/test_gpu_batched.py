@@ -108,6 +108,23 @@ def test_batched_small_shapes(name, T):
     batched_parity(SMALL[name], T)
 
 
+@pytest.mark.parametrize("name", ["ragged_shared", "h8192"])
+def test_identical_tokens_fill_every_group(name):
+    """64 copies of one token: every selected expert's group holds the whole
+    batch (four 16-token passes per expert).  Each token's column goes
+    through the same arithmetic, so all 64 outputs, indices and weights are
+    bit-identical; the first row meets the oracle."""
+    w = SMALL[name]
+    dl = device_layer(w, 0)
+    X = np.repeat(tokens_of(w, dl, 1, start=3), 64, axis=0)
+    out, idx, wts = run_batched(w, dl, X)
+    assert (out == out[0]).all() and (idx == idx[0]).all() and (wts == wts[0]).all()
+    ref = oracle_layer(w, 0, dl.router_host, X[:1], X[:1])
+    check_topk(idx[:1], ref, w.k)
+    err = max_err_ratio(out[:1], ref["out"])
+    assert err.max() <= TOL, err.max()
+
+
 def test_k3_batch64_zipf_layer():
     """The K3-shaped layer at batch 64 with Zipf-skewed routing: every
     token's top-k against the oracle, outputs of 16 sampled tokens."""
