@@ -4,7 +4,8 @@
 //           tokens per fragment), the reduction dimension split KS ways;
 //           partial sums go to the workspace.
 //  topk     one workgroup per token: adds the KS partials in a fixed order,
-//           then the radix top-k + softmax shared with the single-token path.
+//           stages the logits in LDS, then one wave runs the top-k +
+//           softmax shared with the single-token path.
 //  group    one workgroup: a 64-bit token mask per expert gives each
 //           (token, slot) pair its stable rank inside its expert, hence a
 //           counting sort of the pairs by expert (pairs of an expert ordered
