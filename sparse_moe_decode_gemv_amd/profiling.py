@@ -29,6 +29,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(HERE, "csrc", "moe_t1.hip")
+BATCHED_SRC = os.path.join(HERE, "csrc", "moe_batched.hip")
 CALIB_BYTES = 1 << 30
 
 _NAMES = re.compile(r"(k1_router|k1_topk|k2_gateup|k3_slab|k3_down|kb_\w+|"
@@ -40,8 +41,8 @@ def short(name: str) -> str:
     return m.group(1) if m else name[:40]
 
 
-def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def source_digest(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -137,9 +138,11 @@ def _counter_means(path: str, counter: str):
     items = list(disp.values())
     keys = _classify([i[0] for i in items])
     agg = collections.defaultdict(list)
-    for k, (name, v, grid) in zip(keys, items):
+    for k, d, (name, v, grid) in zip(keys, disp.keys(), items):
         if name.startswith("copyBuffer"):
-            k = f"{name} grid={grid}"
+            # copies stay separate: another copy can share the calibration
+            # copy's grid (the grid size is capped for large copies)
+            k = f"{name} grid={grid} dispatch={d}"
         agg[k].append(v)
     return {k: st.mean(v) for k, v in agg.items()}, {k: len(v) for k, v in agg.items()}
 
@@ -164,6 +167,7 @@ def counters(fetch_csv: str, write_csv: str) -> str:
         if k == "k2_gateup (stand-alone)":
             traffic = b
     out.append(f"kernel_source_sha256_16: {source_digest()}")
+    out.append(f"batched_source_sha256_16: {source_digest(BATCHED_SRC)}")
     if traffic is not None:
         out.append(f"traffic_bytes_per_launch: {traffic}")
     return "\n".join(out)

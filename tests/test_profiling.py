@@ -35,3 +35,27 @@ def test_layer_spans_batched_layer_with_rmsnorm_and_foreign_kernel():
 
 def test_no_layer_in_trace():
     assert P.layer_spans(["copyBuffer"], [("", 0, 10)]) == "no complete decode layer in the trace"
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n")
+        for d, name, grid, v in rows:
+            f.write(f'{d},"{name}",{grid},{counter},{v}\n')
+
+
+def test_counter_calibration_uses_the_largest_copy(tmp_path):
+    """Two copies with the same (capped) grid: the 1 GiB calibration copy and
+    a small one.  The scale comes from the 1 GiB copy alone."""
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    rows_f = [(1, "copyBuffer", 131072, 524288.0), (2, "copyBuffer", 131072, 7000.0),
+              (3, "kb_gateup", 768, 1000.0), (4, "kb_gateup", 768, 3000.0)]
+    rows_w = [(1, "copyBuffer", 131072, 1048576.0), (2, "copyBuffer", 131072, 14000.0),
+              (3, "kb_gateup", 768, 10.0), (4, "kb_gateup", 768, 30.0)]
+    _counter_csv(fetch, "FETCH_SIZE", rows_f)
+    _counter_csv(write, "WRITE_SIZE", rows_w)
+    out = P.counters(str(fetch), str(write))
+    assert "fetch_scale: 2.0000" in out and "write_scale: 1.0000" in out
+    # mean of the two launches: 2000 KiB fetched x 2 + 20 KiB written
+    line = [l for l in out.splitlines() if l.startswith("kb_gateup")][0]
+    assert line.split()[-1] == str((2000 * 2 + 20) * 1024)
