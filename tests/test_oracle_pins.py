@@ -237,6 +237,72 @@ def test_far_logit_gets_exactly_zero_weight():
     assert w[list(idx[0]).index(1)] == 0.0
 
 
+# ------------------------------------------------- gaps that gate the checks
+# Hand-worked vectors.  l = [3, 1, 4, 1.5, 9, 2.5] sorted descending is
+# 9, 4, 3, 2.5, 1.5, 1, so the consecutive differences are 5, 1, 0.5, 1, 0.5.
+
+HAND = np.array([3.0, 1.0, 4.0, 1.5, 9.0, 2.5])
+
+
+def test_topk_gap_hand_worked():
+    # k-th minus (k+1)-th largest: k = 1 -> 9 - 4, k = 2 -> 4 - 3, ...
+    want = {1: 5.0, 2: 1.0, 3: 0.5, 4: 1.0, 5: 0.5}
+    for k, g in want.items():
+        assert O.topk_gap(HAND[None, :], k)[0] == g, k
+    assert O.topk_gap(HAND[None, :], 6)[0] == np.inf      # k = E: no (k+1)-th
+    # exact ties at the boundary give a zero gap; ties inside the top-k do not
+    l = np.array([[2.0, 5.0, 5.0, 1.0]])
+    assert O.topk_gap(l, 1)[0] == 0.0
+    assert O.topk_gap(l, 2)[0] == 3.0
+    assert O.topk_gap(l, 3)[0] == 1.0
+    # per token, independent of the order of the experts
+    rows = np.stack([HAND, HAND[::-1], np.roll(HAND, 2)])
+    assert O.topk_gap(rows, 2).tolist() == [1.0, 1.0, 1.0]
+    two = np.stack([HAND, np.array([0.0, 10.0, 9.75, -1.0, 3.0, 2.0])])
+    assert O.topk_gap(two, 2).tolist() == [1.0, 6.75]
+
+
+def test_adjacent_gaps_hand_worked():
+    # smallest consecutive difference among the k+1 largest
+    want = {1: 5.0, 2: 1.0, 3: 0.5, 4: 0.5, 5: 0.5}
+    for k, g in want.items():
+        assert O.adjacent_gaps(HAND[None, :], k)[0] == g, k
+    # k = E: the ordering of all E logits matters, so all of them are compared
+    assert O.adjacent_gaps(HAND[None, :], 6)[0] == 0.5
+    # a close pair below the (k+1)-th logit is ignored ...
+    l = np.array([[10.0, 8.0, 6.0, 5.9, 0.0]])
+    assert O.adjacent_gaps(l, 1)[0] == 2.0
+    assert O.adjacent_gaps(l, 2)[0] == 2.0
+    assert O.adjacent_gaps(l, 3)[0] == pytest.approx(0.1, abs=1e-15)
+    # ... but a close pair at the k-th / (k+1)-th boundary counts
+    l = np.array([[10.0, 8.0, 7.99, -3.0]])
+    assert O.adjacent_gaps(l, 2)[0] == pytest.approx(0.01, abs=1e-15)
+    assert O.adjacent_gaps(l, 1)[0] == 2.0
+    # ties inside the top k make the order ambiguous: zero gap
+    assert O.adjacent_gaps(np.array([[2.0, 5.0, 5.0, 1.0]]), 1)[0] == 0.0
+    # one expert: nothing to order
+    assert O.adjacent_gaps(np.array([[1.5]]), 1)[0] == np.inf
+
+
+def test_gaps_agree_with_brute_force_over_subsets():
+    """topk_gap is the margin by which the chosen set wins: the smallest
+    selected logit minus the largest unselected one.  adjacent_gaps is the
+    smallest difference between any two of the k+1 largest logits (not only
+    neighbours, which gives the same minimum).  Both from the brute-force
+    top-k, which shares no code with the oracle's sort."""
+    rng = np.random.default_rng(41)
+    for _ in range(200):
+        E = int(rng.integers(2, 9))
+        l = rng.integers(-20, 21, E).astype(np.float64) / 4
+        for k in range(1, E):
+            S = _brute_topk(l, k)
+            rest = [e for e in range(E) if e not in S]
+            assert O.topk_gap(l[None, :], k)[0] == min(l[S]) - max(l[rest])
+            S1 = _brute_topk(l, k + 1)
+            want = min(abs(l[a] - l[b]) for a, b in itertools.combinations(S1, 2))
+            assert O.adjacent_gaps(l[None, :], k)[0] == want
+
+
 # ------------------------------------------------------------------ SiLU
 
 def test_silu_textbook_identities():
@@ -273,6 +339,62 @@ def test_expert_closed_form_all_ones():
     y = O.expert_ffn(x, _const_expert(H, F, 0x22, 0x7B, s_d, s_u=0x7D))
     g, u = 2.0 ** -4 * x.sum(), 2.0 ** -2 * x.sum()
     assert np.allclose(y, 2.0 ** -7 * F * (g / (1 + math.exp(-g)) * u), rtol=1e-14, atol=0)
+
+
+def test_expert_activation_closed_form():
+    """The gated hidden vector alone: with every element 1.0, distinct gate
+    and up scales and a different code per gate row, row f of a is
+    silu(c_f 2^-4 sum x) * 2^-2 sum x.  Swapping gate and up (silu of the up
+    projection), dropping the gating or mixing up rows fails."""
+    H, F = 64, 32
+    rng = np.random.default_rng(16)
+    x = rng.integers(-3, 4, H).astype(np.float64) / 4
+    while abs(x.sum()) < 1:
+        x = rng.integers(-3, 4, H).astype(np.float64) / 4
+    ex = _const_expert(H, F, 0x22, 0x7B, 0x78, s_u=0x7D)
+    # gate row f: both nibbles code c in {0.5, 1, 1.5, 2} (codes 1, 2, 3, 4)
+    codes = [0x11, 0x22, 0x33, 0x44]
+    vals = [0.5, 1.0, 1.5, 2.0]
+    g_codes = ex["gate"][0].copy()
+    for f in range(F):
+        g_codes[f, :] = codes[f % 4]
+    ex["gate"] = (g_codes, ex["gate"][1])
+    a = O.expert_activation(x, ex)
+    s = x.sum()
+    for f in range(F):
+        g = vals[f % 4] * 2.0 ** -4 * s
+        want = g / (1 + math.exp(-g)) * (2.0 ** -2 * s)
+        assert a[f] == pytest.approx(want, rel=1e-14, abs=0), f
+
+
+def test_expert_activation_brute_force_and_down_projection():
+    """On random bytes: each row of a from scalar loops over the code bytes
+    (values from the hand table in tests/golden/), and D a reproduces the
+    expert output."""
+    e2m1, e8m0, _ = _formats()
+    H, F = 64, 32
+    rng = np.random.default_rng(17)
+    ex = _rand_expert(rng, H, F)
+    table = np.array([0x77, 0x7B, 0x7F, 0x80], np.uint8)   # scale bytes of the hand table
+    for m in ("gate", "up", "down"):
+        ex[m] = (ex[m][0], table[rng.integers(0, 4, ex[m][1].shape)])
+    x = rng.standard_normal(H)
+
+    def row_dot(codes, scales, r):
+        acc = 0.0
+        for i in range(H // 2):
+            b = int(codes[r, i])
+            sc = e8m0[int(scales[r, (2 * i) // 32])]
+            acc += e2m1[b & 0xF] * sc * x[2 * i] + e2m1[b >> 4] * sc * x[2 * i + 1]
+        return acc
+
+    a = O.expert_activation(x, ex)
+    for f in range(F):
+        g = row_dot(*ex["gate"], f)
+        u = row_dot(*ex["up"], f)
+        assert a[f] == pytest.approx(g / (1 + math.exp(-g)) * u, rel=1e-12, abs=1e-15), f
+    y = O.expert_ffn(x, ex)
+    assert np.allclose(O.mx_decode(*ex["down"]) @ a, y, rtol=1e-13, atol=1e-15)
 
 
 def _rand_expert(rng, H, F):
