@@ -3,7 +3,7 @@
 
 A step is one decode layer (router GEMV, top-k + softmax, gate/up with SiLU
 gating, down projection, weighted combine with the shared expert, residual
-add) on one token of the chosen workload, through the C ABI of
+add) on one batch of the chosen workload, through the C ABI of
 libmoe_decode.so.  Default workload: the K3-shaped batch-1 layer (hidden 7168,
 896 routed experts, top-16, expert FFN 2048, one shared expert of FFN 2048).
 
@@ -13,11 +13,22 @@ Measurement
   16 distinct tokens are rotated over them, so consecutive steps stream
   different bytes and the 256 MB Infinity Cache cannot serve a step from the
   previous one.
-* Steps are captured into HIP graphs of 16 layer calls and replayed; the K
-  timed steps are bracketed by a device synchronisation and HIP events on
-  the stream the kernels run on.
-* The dominant kernel (routed gate/up) is also timed on its own, in graphs of
-  16 launches over the same rotation, for the roofline figure.
+* The K timed steps are captured into HIP graphs (one graph of all K steps
+  when K <= 256, else graphs of 64) and replayed; a device synchronisation
+  and HIP events on the stream the kernels run on bracket them.  p10/p50/p90
+  come from the per-replay times.
+* Before the timed replays the GPU is settled: after the W warmup steps and
+  the graph's upload, the same graph is replayed (untimed) until SETTLE_S of
+  back-to-back work has run.  Right after a capture or an idle spell the
+  first ~10 ms of replays run up to ~12 % slower than the steady state (the
+  GPU's clocks and power state adjust), which a short timed region would
+  otherwise measure instead of the layer.  The JSON reports the settle work.
+* Kernel pass: the same rotation through moe_decode_layer_timed, which
+  launches the same kernels with HIP recording each kernel's own start and
+  end; it gives the kernels per layer, their mean durations, the idle time
+  between them, and the dominant kernel's duration for the roofline.
+* A plain streaming read of 4 GiB gives this GPU's measured read ceiling as
+  context for the 8 TB/s peak.
 * The fp64 CPU oracle is timed on a bounded sample of the same workload
   (cpu_baseline leg; the oracle is test infrastructure and is used here only
   as that reported baseline).
@@ -27,7 +38,6 @@ Prints ONE JSON line on stdout; details go to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -39,10 +49,19 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = "µs per MoE decode layer (batch 1) and achieved HBM GB/s as fraction of peak"
-ROT_TOKENS = 16                 # distinct tokens in the rotation (= steps per graph)
+ROT_TOKENS = 16                 # distinct batches in the rotation
+ONE_GRAPH_MAX = 256             # up to this many steps are captured as one graph
+GRAPH_STEPS = 64                # steps per graph beyond that
+SETTLE_S = 0.15                 # untimed back-to-back replays before the timed ones
 CALIB_BYTES = 1 << 30           # size of the counter-calibration copy
-COUNTERS = os.path.join(ROOT, "profiles", "k2_gateup_k3_batch1_counters.txt")
-KERNEL_SRC = os.path.join(ROOT, "sparse_moe_decode_gemv_amd", "csrc", "moe_t1.hip")
+STREAM_BYTES = 4 << 30          # streaming-read ceiling buffer
+PROFILES = os.path.join(ROOT, "profiles")
+COUNTERS = {  # workload -> committed rocprofv3 counter summary
+    "k3_batch1": os.path.join(PROFILES, "k2_gateup_k3_batch1_counters.txt"),
+    "k3_batch64_zipf": os.path.join(PROFILES, "kb_gateup_kb_down_k3_batch64_counters.txt"),
+}
+T1_KERNELS = ["k1_router", "k2_gateup", "k3_down_combine"]
+TB_KERNELS = ["kb_router", "kb_topk", "kb_group", "kb_gateup", "kb_down", "kb_combine"]
 
 
 def log(*a):
@@ -66,34 +85,52 @@ def layer_bytes(w, touched=None) -> int:
     return w.T * (2 * w.H + 2 * w.H) + 2 * w.E * w.H + n * expert + shared + gamma
 
 
-def gateup_bytes(w) -> int:
-    """Compulsory bytes of one routed gate/up launch: k experts' gate and up
-    matrices, x in, fp32 activations out."""
+def gateup_bytes_in_layer(w, touched=None) -> int:
+    """Compulsory bytes of the layer's gate/up kernel: gate and up matrices of
+    every touched routed expert and of the shared expert, x in, the router
+    logits in (batch 1: the selection runs in this kernel), and the gated
+    activations out (two bf16 parts per element)."""
+    n = w.T * w.k if touched is None else touched
+    mats = n * 2 * mx_bytes(w.F, w.H) + w.S * 2 * mx_bytes(w.Fs, w.H)
+    logits = 4 * w.E if w.T == 1 else 0
+    acts = 2 * 2 * w.T * (w.k * w.F + w.S * w.Fs)
+    return mats + 2 * w.T * w.H + logits + acts
+
+
+def gateup_bytes_standalone(w) -> int:
+    """The exported routed gate/up: k experts' gate and up matrices, x in,
+    fp32 activations out."""
     return w.k * 2 * mx_bytes(w.F, w.H) + 2 * w.H + 4 * w.k * w.F
 
 
-def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def measured_traffic(workload: str, kernel_key: str):
+    """HBM bytes per launch of one kernel from the committed rocprofv3 counter
+    summary, or None if there is none or it was taken on other kernel
+    sources."""
+    from sparse_moe_decode_gemv_amd import profiling as P
+    path = COUNTERS.get(workload)
+    if not path or not os.path.exists(path):
+        return None
+    vals, table = P.read_counter_summary(path)
+    if vals.get("kernel_source_sha256_16") != P.source_digest():
+        return None
+    if kernel_key.startswith("kb_") and vals.get("batched_source_sha256_16") != P.source_digest(P.BATCHED_SRC):
+        return None
+    return table.get(kernel_key)
 
 
-def measured_traffic():
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter
-    summary, or None if it is missing or was taken on another kernel source."""
-    if not os.path.exists(COUNTERS):
-        return None
-    vals = {}
-    with open(COUNTERS) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != source_digest():
-        return None
+def cpu_info():
+    visible = len(os.sched_getaffinity(0))
+    model = "unknown"
     try:
-        return int(vals["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return visible, model
 
 
 # ----------------------------------------------------------------- CPU leg
@@ -108,7 +145,11 @@ def cpu_baseline(w, router_hosts, toks, budget_s: float):
     except ImportError:                      # pragma: no cover
         threadpool_limits = None
 
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    visible, model = cpu_info()
+    # the host's CPU share for one GPU (the environment's thread setting), at
+    # most what the process may run on
+    share = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    cores = max(1, min(visible, share))
     pool = ThreadPoolExecutor(max_workers=cores)
     hx = G.HostExperts(w, 0)
     shared = hx.shared()
@@ -130,16 +171,22 @@ def cpu_baseline(w, router_hosts, toks, budget_s: float):
         if lim is not None:
             lim.unregister()
         pool.shutdown()
-    # one token per call: per layer at batch 1, per token and layer otherwise
     unit = "µs per layer" if w.T == 1 else "µs per token per layer"
     return {"value": round(spent / done * 1e6, 1), "unit": unit, "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cores_visible": visible, "cpu_model": model,
             "sample": f"{done} single token(s) of {w.name} through one layer (weight set 0), "
-                      f"fp64 numpy oracle, {cores} worker threads, BLAS limited to 1 thread; "
+                      f"fp64 numpy oracle on {cores} worker threads (the host's CPU share for "
+                      f"one GPU; {visible} visible), BLAS limited to 1 thread per worker; "
                       f"expert bytes generated before the clock starts"}
 
 
 # ------------------------------------------------------------------ GPU leg
+def percentiles(v):
+    import numpy as np
+    q = np.percentile(np.asarray(v), [10, 50, 90])
+    return {"p10": round(float(q[0]), 3), "p50": round(float(q[1]), 3), "p90": round(float(q[2]), 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +200,9 @@ def main():
                     help="launch every step directly (no graph), e.g. under counter profiling")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed steps (no kernel pass, stand-alone gate/up or "
+                         "streaming read), e.g. under counter profiling")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -230,8 +280,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # ---- the timed steps
     K = args.steps
-    per_rep = []
+    per_rep, rep_steps, settle = [], 0, None
     if args.eager:
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -242,21 +293,32 @@ def main():
         torch.cuda.synchronize()
         total_ms = ev0.elapsed_time(ev1)
     else:
-        def capture(n):
+        def capture(first, n):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for i in range(n):
+                for i in range(first, first + n):
                     step(i)
             return g
-        full, rem = divmod(K, ROT_TOKENS)
-        g_full = capture(ROT_TOKENS) if full else None
-        g_rem = capture(rem) if rem else None
+        rep_steps = K if K <= ONE_GRAPH_MAX else GRAPH_STEPS
+        full, rem = divmod(K, rep_steps)
+        # rep_steps is a multiple of the rotation or covers K: every replay
+        # walks the same rotation
+        g_full = capture(0, rep_steps) if full else None
+        g_rem = capture(0, rem) if rem else None
         for g in (g_full, g_rem):             # first replay uploads the graph: untimed
             if g is not None:
                 g.replay()
         torch.cuda.synchronize()
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(full + 2)]
-        torch.cuda.synchronize()
+        # settle (untimed): replays back to back until SETTLE_S has passed
+        g_settle = g_full if g_full is not None else g_rem
+        settle_steps, t_settle = 0, time.perf_counter()
+        while time.perf_counter() - t_settle < SETTLE_S:
+            for _ in range(4):
+                g_settle.replay()
+            settle_steps += 4 * (rep_steps if g_full is not None else rem)
+            torch.cuda.synchronize()
+        settle = {"steps": settle_steps, "seconds": round(time.perf_counter() - t_settle, 3)}
         evs[0].record(stream)
         for r in range(full):
             g_full.replay()
@@ -266,7 +328,7 @@ def main():
         evs[-1].record(stream)
         torch.cuda.synchronize()
         total_ms = evs[0].elapsed_time(evs[-1])
-        per_rep = [evs[r].elapsed_time(evs[r + 1]) / ROT_TOKENS for r in range(full)]
+        per_rep = [evs[r].elapsed_time(evs[r + 1]) * 1e3 / (rep_steps * nlayers) for r in range(full)]
 
     ms_per_step = total_ms / K
     us_layer = ms_per_step * 1e3 / nlayers
@@ -275,80 +337,175 @@ def main():
     log(f"[bench] {K} steps in {total_ms:.3f} ms: {us_layer:.2f} µs/layer, "
         f"{layer_gbps:.0f} GB/s algorithmic ({lb} B/layer), "
         f"{layer_gbps / PEAK_HBM_GBPS:.3f} of peak")
-    if per_rep:
-        q = np.percentile(np.array(per_rep) * 1e3 / nlayers, [10, 50, 90])
-        log(f"[bench] per-graph µs/layer p10 {q[0]:.2f} p50 {q[1]:.2f} p90 {q[2]:.2f}")
 
-    # ---- dominant kernel alone: routed gate/up over the same rotation
-    roofline = None
-    if not stack and T == 1:
-        k = w.k
-        idx = torch.empty((nsets, ROT_TOKENS, k), dtype=torch.int32, device="cuda")
-        tw = torch.empty((nsets, ROT_TOKENS, k), dtype=torch.float32, device="cuda")
-        for s in range(nsets):
-            for t in range(ROT_TOKENS):
-                M.router_topk(shape, xs[t], sets[s][0].router, 1, idx[s, t:t + 1],
-                              tw[s, t:t + 1], None, ws)
-        act = torch.empty((k, w.F), dtype=torch.float32, device="cuda")
-
-        def gu(i):
-            s, t = i % nsets, i % ROT_TOKENS
-            M.expert_gateup(shape, wts[s][0], xs[t], idx[s, t:t + 1], 1, act, ws)
-
-        for i in range(ROT_TOKENS):
-            gu(i)
-        n_launch = max(ROT_TOKENS, (K // ROT_TOKENS) * ROT_TOKENS)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        if args.eager:
+    # ---- spread over graph replays (extra untimed replays when the timed
+    # region holds fewer than 8)
+    spread = None
+    if not args.eager:
+        src = f"{len(per_rep)} timed replays of {rep_steps} steps"
+        if len(per_rep) < 8 and g_full is not None:
+            extra = [torch.cuda.Event(enable_timing=True) for _ in range(33)]
             torch.cuda.synchronize()
-            e0.record(stream)
-            for i in range(n_launch):
+            extra[0].record(stream)
+            for r in range(32):
+                g_full.replay()
+                extra[r + 1].record(stream)
+            torch.cuda.synchronize()
+            per_rep = per_rep + [extra[r].elapsed_time(extra[r + 1]) * 1e3 / (rep_steps * nlayers)
+                                 for r in range(32)]
+            src += " + 32 untimed replays of the same graph"
+        if per_rep:
+            spread = {"unit": "µs/layer", **percentiles(per_rep), "source": src}
+            log(f"[bench] per-replay µs/layer p10 {spread['p10']} p50 {spread['p50']} "
+                f"p90 {spread['p90']} ({src})")
+
+    kernels = roofline = standalone = ceiling = None
+    if not args.no_extras:
+        # ---- kernel pass: every kernel of a layer timed by HIP itself
+        names = T1_KERNELS if T == 1 else TB_KERNELS
+        nk_max = len(names)
+        n_prof = min(64, max(16, K))
+        # the stack's layers are the batch-1 layer's kernels (RMSNorm runs in
+        # the router's prologue); they are timed as plain layers here
+        evp = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(nk_max)] for _ in range(n_prof)]
+        for row in evp:                       # create the events before handing them over
+            for a, b in row:
+                a.record(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        nks = []
+        for i in range(n_prof):
+            s, t = i % nsets, i % ROT_TOKENS
+            lay = i % nlayers
+            nks.append(M.decode_layer_timed(shape, wts[s][lay], xs[t], xs[t], outs[t], T, None,
+                                            None, ws, evp[i]))
+        torch.cuda.synchronize()
+        assert len(set(nks)) == 1 and nks[0] == nk_max, nks
+        dur = np.array([[a.elapsed_time(b) * 1e3 for a, b in row] for row in evp])
+        gaps = np.array([[row[j][1].elapsed_time(row[j + 1][0]) * 1e3 for j in range(nk_max - 1)]
+                         for row in evp])
+        span = np.array([row[0][0].elapsed_time(row[-1][1]) * 1e3 for row in evp])
+        kernels = {"per_layer": nk_max, "names": names,
+                   "mean_us": {n: round(float(dur[:, j].mean()), 3) for j, n in enumerate(names)},
+                   "idle_between_kernels_us": round(float(gaps.sum(axis=1).mean()), 3),
+                   "gap_us": [round(float(g), 3) for g in gaps.mean(axis=0)],
+                   "layer_span_us": round(float(span.mean()), 3),
+                   "source": f"moe_decode_layer_timed over {n_prof} layers of the same rotation, "
+                             f"eager; each kernel's start and end recorded by HIP (the eager "
+                             f"launches leave gaps a graph does not have)"}
+        if not stack:
+            # in the graph: the timed µs per layer minus the kernels' own time
+            kernels["graph_idle_us_per_layer"] = round(us_layer - float(dur.mean(axis=0).sum()), 3)
+        log(f"[bench] kernels per layer {nk_max}: " +
+            ", ".join(f"{n} {kernels['mean_us'][n]:.2f} µs" for n in names) +
+            f"; idle between them {kernels['idle_between_kernels_us']:.2f} µs; "
+            f"span {kernels['layer_span_us']:.2f} µs")
+
+        # ---- roofline of the dominant kernel as it runs in the layer
+        kname = "k2_gateup" if T == 1 else "kb_gateup"
+        j = names.index(kname)
+        kb = gateup_bytes_in_layer(w, touched)
+        us_k = float(dur[:, j].mean())
+        ach = kb / (us_k * 1e-6) / 1e9
+        key = "k2_gateup (in layer)" if T == 1 else "kb_gateup"
+        traffic = measured_traffic(w.name, key)
+        roofline = {"bound": "hbm", "kernel": f"{kname} in the layer (gate/up + SiLU gating of "
+                                              f"the selected and shared experts)",
+                    "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                    "bytes_per_launch": kb, "us_per_launch": round(us_k, 3)}
+        log(f"[bench] {kname} in the layer: {us_k:.2f} µs/launch, {ach:.0f} GB/s "
+            f"({kb} B/launch), traffic {traffic}")
+
+        # ---- the exported routed gate/up alone (batch 1)
+        if T == 1 and not stack:
+            idx = torch.empty((nsets, ROT_TOKENS, w.k), dtype=torch.int32, device="cuda")
+            tw = torch.empty((nsets, ROT_TOKENS, w.k), dtype=torch.float32, device="cuda")
+            for s in range(nsets):
+                for t in range(ROT_TOKENS):
+                    M.router_topk(shape, xs[t], sets[s][0].router, 1, idx[s, t:t + 1],
+                                  tw[s, t:t + 1], None, ws)
+            act = torch.empty((w.k, w.F), dtype=torch.float32, device="cuda")
+
+            def gu(i):
+                s, t = i % nsets, i % ROT_TOKENS
+                M.expert_gateup(shape, wts[s][0], xs[t], idx[s, t:t + 1], 1, act, ws)
+
+            for i in range(ROT_TOKENS):
                 gu(i)
-            e1.record(stream)
-        else:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for i in range(ROT_TOKENS):
                     gu(i)
             g.replay()
             torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 8
             e0.record(stream)
-            for _ in range(n_launch // ROT_TOKENS):
+            for _ in range(reps):
                 g.replay()
             e1.record(stream)
+            torch.cuda.synchronize()
+            us_sa = e0.elapsed_time(e1) * 1e3 / (reps * ROT_TOKENS)
+            kb_sa = gateup_bytes_standalone(w)
+            standalone = {"kernel": "k2_gateup via moe_expert_gateup (16 routed experts given, "
+                                    "no selection, no shared expert)",
+                          "us_per_launch": round(us_sa, 3), "bytes_per_launch": kb_sa,
+                          "achieved": round(kb_sa / (us_sa * 1e-6) / 1e9, 1),
+                          "traffic": measured_traffic(w.name, "k2_gateup (stand-alone)")}
+            log(f"[bench] routed gate/up alone: {us_sa:.2f} µs/launch, "
+                f"{standalone['achieved']:.0f} GB/s")
+
+        # ---- measured streaming-read ceiling
+        buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda")
+        sink = torch.empty(M.MOE_STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
+        for _ in range(2):
+            M.stream_read(buf, sink)
+        reps = 8
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        us_k2 = e0.elapsed_time(e1) * 1e3 / n_launch
-        kb = gateup_bytes(w)
-        ach = kb / (us_k2 * 1e-6) / 1e9
-        # the counter summary covers the K3 batch-1 workload's gate/up launch only
-        traffic = measured_traffic() if w.name == "k3_batch1" else None
-        roofline = {"bound": "hbm", "kernel": "k2_gateup (routed gate/up + SiLU gating)",
-                    "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                    "bytes_per_launch": kb, "us_per_launch": round(us_k2, 3)}
-        log(f"[bench] gate/up kernel alone: {us_k2:.2f} µs/launch, {ach:.0f} GB/s "
-            f"({kb} B/launch), traffic {traffic}")
+        e0.record(stream)
+        for _ in range(reps):
+            M.stream_read(buf, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbps = STREAM_BYTES * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        ceiling = {"kernel": "stream_read_kernel (moe_stream_read, 16-byte nontemporal loads)",
+                   "bytes": STREAM_BYTES, "achieved": round(gbps, 1), "unit": "GB/s",
+                   "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                   "layer_frac_of_ceiling": round(layer_gbps / gbps, 4)}
+        del buf
+        log(f"[bench] streaming read of {STREAM_BYTES >> 30} GiB: {gbps:.0f} GB/s "
+            f"({gbps / PEAK_HBM_GBPS:.3f} of peak); layer at {layer_gbps / gbps:.3f} of it")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host ...")
         cpu = cpu_baseline(w, [d.router_host for d in sets[0]],
                            [b[0] for b in toks_host[:8]], args.cpu_seconds)
-        log(f"[bench] oracle: {cpu['value']} {cpu['unit']} on {cpu['cores']} threads")
+        log(f"[bench] oracle: {cpu['value']} {cpu['unit']} on {cpu['cores']} threads "
+            f"({cpu['cpu_model']})")
 
     line = {
         "metric": METRIC, "value": round(us_layer, 3), "unit": "µs/layer",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "settle_untimed": settle,
+        "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4xbf16-fp32acc", "data": "synthetic",
         "config": {"workload": f"{w.name}: T={w.T} H={w.H} E={w.E} top-{w.k} F={w.F} "
                                f"shared={w.S}x{w.Fs} layers={nlayers}",
                    "global_batch": w.T, "weight_sets": nsets,
-                   "timing": "eager" if args.eager else "hipGraph of 16 steps"},
+                   "timing": "eager" if args.eager else
+                   f"hipGraph replays of {rep_steps} steps"},
         "layer_tokens_per_s": round(T * 1e6 / us_layer, 1),
         "layer_hbm": {"bytes": lb, "achieved": round(layer_gbps, 1), "unit": "GB/s",
                       "frac": round(layer_gbps / PEAK_HBM_GBPS, 4)},
+        "spread": spread,
+        "kernels": kernels,
         "roofline": roofline,
+        "gateup_standalone": standalone,
+        "stream_read_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line, ensure_ascii=False), flush=True)

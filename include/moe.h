@@ -66,6 +66,8 @@ extern "C" {
 #endif
 
 #define MOE_WS_COUNTER_BYTES 256
+#define MOE_MAX_LAYER_KERNELS 8    /* kernels one moe_decode_layer call launches, at most */
+#define MOE_STREAM_SINK_WORDS 4096 /* uint32 words moe_stream_read may write to `sink` */
 
 typedef enum {
   MOE_OK = 0,
@@ -143,6 +145,33 @@ int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const u
                      const uint16_t* residual, uint16_t* out, int32_t n_tokens,
                      int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* Measurement variant of moe_decode_layer: the same validation, kernels and
+ * results, but kernel i of the call is launched with hipExtLaunchKernel so
+ * that HIP records when it starts and ends executing on the GPU (the pages
+ * count kernels per decoder layer and the gaps between them: page
+ * "AI手搓1.2万行代码榨干GB300!…", section 02).
+ * events      host array of 2 * max_kernels hipEvent_t handles created by
+ *             the caller with timing enabled: kernel i records events[2i]
+ *             at its start and events[2i+1] at its end; kernels past
+ *             max_kernels (0 <= max_kernels <= MOE_MAX_LAYER_KERNELS)
+ *             launch untimed
+ * n_kernels   host int32 out: number of kernels the call launched (3 for
+ *             one token, 6 for 2..64 tokens)
+ * The events are recorded eagerly, so the call is not meant for graph
+ * capture; read them after synchronising the stream. */
+int moe_decode_layer_timed(const moe_shape* shape, const moe_layer_weights* w,
+                           const uint16_t* x, const uint16_t* residual, uint16_t* out,
+                           int32_t n_tokens, int32_t* topk_idx_out, float* topk_w_out,
+                           void* ws, size_t ws_bytes, void* stream, void* const* events,
+                           int32_t max_kernels, int32_t* n_kernels);
+
+/* Measurement helper: one plain streaming read of `bytes` bytes at `buf`
+ * (16-byte aligned, bytes a multiple of 16) with 16-byte nontemporal loads
+ * over the whole chip, the rate a weight stream can reach on this GPU.
+ * sink: device uint32 [MOE_STREAM_SINK_WORDS]; each workgroup stores the xor
+ * of the words it read (contents otherwise meaningless). */
+int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* A stack of decode layers run back to back.  Per layer l:
  *   xn = bf16(h * gamma_l / sqrt(mean(h^2) + eps));  h = bf16(h + MoE_l(xn))

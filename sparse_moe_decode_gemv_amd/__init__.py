@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(HERE, "libmoe_decode.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_MAX_LAYER_KERNELS = 8
+MOE_STREAM_SINK_WORDS = 4096
 
 
 class MoeError(RuntimeError):
@@ -58,6 +60,11 @@ _SIG = {
                           ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_group_by_expert": ([_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                              ctypes.c_size_t, _P]),
+    "moe_decode_layer_timed": ([ctypes.POINTER(MoeShape), ctypes.POINTER(MoeLayerWeights), _P,
+                                _P, _P, ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P,
+                                ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
+                                ctypes.POINTER(ctypes.c_int32)]),
+    "moe_stream_read": ([_P, ctypes.c_size_t, _P, _P]),
 }
 
 
@@ -163,3 +170,23 @@ def group_by_expert(topk_idx, n_tokens, top_k, n_experts, offsets, pairs, ws, st
     _check("moe_group_by_expert", lib().moe_group_by_expert(
         _ptr(topk_idx), n_tokens, top_k, n_experts, _ptr(offsets), _ptr(pairs), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def decode_layer_timed(shape, weights, x, residual, out, n_tokens, topk_idx_out, topk_w_out, ws,
+                       events, stream=None) -> int:
+    """``events``: list of (start, stop) torch.cuda.Event pairs (timing
+    enabled, already created); returns the number of kernels launched."""
+    n = len(events)
+    handles = (ctypes.c_void_p * (2 * n))(*[h for a, b in events for h in (a.cuda_event,
+                                                                          b.cuda_event)])
+    nk = ctypes.c_int32(0)
+    _check("moe_decode_layer_timed", lib().moe_decode_layer_timed(
+        ctypes.byref(shape), ctypes.byref(weights), _ptr(x), _ptr(residual), _ptr(out), n_tokens,
+        _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream), handles, n, ctypes.byref(nk)))
+    return nk.value
+
+
+def stream_read(buf, sink, stream=None):
+    _check("moe_stream_read", lib().moe_stream_read(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))

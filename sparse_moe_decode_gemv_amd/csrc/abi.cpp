@@ -216,14 +216,7 @@ uint16_t* xn_tb(const moe_shape* s, void* ws, int T) { return (uint16_t*)((char*
 
 // One full single-token layer: K1a (router), K2 (top-k, shared + routed
 // gate/up), K3 (down of every slot + combine) on one stream.
-int run_layer_t1(LayerT1& L, hipStream_t st) {
-  hipError_t e = moe::launch_router_t1(L, st);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  const uint16_t* xin = L.gamma ? L.xn : L.x;
-  e = moe::launch_gateup_t1(L, xin, nullptr, nullptr, true, st);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_down_combine_t1(L, st));
-}
+int run_layer_t1(LayerT1& L, hipStream_t st) { return hip_status(moe::launch_layer_t1(L, st)); }
 
 // One batched layer: router, top-k, grouping, gate/up, down, combine.
 int run_layer_tb(LayerTB& L, hipStream_t st) {
@@ -312,10 +305,14 @@ int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const 
   return hip_status(moe::launch_gateup_t1(L, x, topk_idx, act, false, (hipStream_t)stream));
 }
 
-int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
-                     const uint16_t* residual, uint16_t* out, int32_t n_tokens,
-                     int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_layer(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
+                 const uint16_t* residual, uint16_t* out, int32_t n_tokens,
+                 int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                 void* stream, moe::KernelTimer* timer) {
   int rc;
   if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
   if (n_tokens == 0) return MOE_OK;
@@ -335,6 +332,7 @@ int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const u
     L.out = out;
     L.idx_out = topk_idx_out;
     L.w_out = topk_w_out;
+    L.timer = timer;
     return run_layer_t1(L, st);
   }
   LayerTB L = make_layer_tb(shape, w, ws, n_tokens);
@@ -343,7 +341,46 @@ int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const u
   L.out = out;
   L.idx_out = topk_idx_out;
   L.w_out = topk_w_out;
+  L.timer = timer;
   return run_layer_tb(L, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
+                     const uint16_t* residual, uint16_t* out, int32_t n_tokens,
+                     int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return decode_layer(shape, w, x, residual, out, n_tokens, topk_idx_out, topk_w_out, ws,
+                      ws_bytes, stream, nullptr);
+}
+
+int moe_decode_layer_timed(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
+                           const uint16_t* residual, uint16_t* out, int32_t n_tokens,
+                           int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                           void* stream, void* const* events, int32_t max_kernels,
+                           int32_t* n_kernels) {
+  if (!events || max_kernels < 0 || max_kernels > MOE_MAX_LAYER_KERNELS || !n_kernels)
+    return MOE_ERR_INVALID_ARG;
+  hipEvent_t start[MOE_MAX_LAYER_KERNELS], stop[MOE_MAX_LAYER_KERNELS];
+  for (int i = 0; i < max_kernels; ++i) {
+    start[i] = (hipEvent_t)events[2 * i];
+    stop[i] = (hipEvent_t)events[2 * i + 1];
+    if (!start[i] || !stop[i]) return MOE_ERR_INVALID_ARG;
+  }
+  moe::KernelTimer tm{start, stop, max_kernels, 0};
+  *n_kernels = 0;
+  const int rc = decode_layer(shape, w, x, residual, out, n_tokens, topk_idx_out, topk_w_out, ws,
+                              ws_bytes, stream, &tm);
+  if (rc == MOE_OK) *n_kernels = tm.used;
+  return rc;
+}
+
+int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || !aligned16(buf) || (bytes & 15u)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_stream_read(buf, bytes, sink, (hipStream_t)stream));
 }
 
 int moe_decode_stack(const moe_shape* shape, const moe_layer_weights* layers,
@@ -404,7 +441,10 @@ int moe_group_by_expert(const int32_t* topk_idx, int32_t n_tokens, int32_t top_k
   if (n_tokens == 0) return MOE_OK;
   if (!topk_idx || !offsets || !pairs) return MOE_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  // the tables start after the counter head, as in the layer's own layout,
+  // so that the counters other calls rely on stay at zero
   Carver c;
+  c.take(MOE_WS_COUNTER_BYTES);
   const WsGroup G = ws_group(c, n_experts, n_tokens, top_k);
   if (c.o > ws_bytes) return MOE_ERR_WORKSPACE;
   LayerTB L{};

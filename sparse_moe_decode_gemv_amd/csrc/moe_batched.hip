@@ -812,17 +812,17 @@ constexpr int kNumCUs = 256;
 hipError_t launch_router_tb(const LayerTB& L, hipStream_t s) {
   const int n_et = (L.E + kTileRows - 1) / kTileRows;
   const int nw = n_et * L.KS;
-  hipLaunchKernelGGL(kb_router, dim3((nw + kWv - 1) / kWv), dim3(kBlk), 0, s, L, n_et);
+  MOE_LAUNCH(L.timer, kb_router, dim3((nw + kWv - 1) / kWv), dim3(kBlk), 0, s, L, n_et);
   return hipPeekAtLastError();
 }
 
 hipError_t launch_topk_tb(const LayerTB& L, hipStream_t s) {
-  hipLaunchKernelGGL(kb_topk, dim3(L.T), dim3(kTopkBlock), 0, s, L);
+  MOE_LAUNCH(L.timer, kb_topk, dim3(L.T), dim3(kTopkBlock), 0, s, L);
   return hipPeekAtLastError();
 }
 
 hipError_t launch_group_tb(const LayerTB& L, hipStream_t s) {
-  hipLaunchKernelGGL(kb_group, dim3(1), dim3(kGroupBlock), 0, s, L);
+  MOE_LAUNCH(L.timer, kb_group, dim3(1), dim3(kGroupBlock), 0, s, L);
   return hipPeekAtLastError();
 }
 
@@ -831,32 +831,32 @@ hipError_t launch_gateup_tb(const LayerTB& L, hipStream_t s) {
   // every workgroup resident at once (items are dealt out round-robin)
   const dim3 g512(kNumCUs * kGroupedBlocksPerCU512);
   if (L.H == 7168)
-    hipLaunchKernelGGL((kb_gateup<512, 14>), g512, dim3(kBlk), 0, s, L);
+    MOE_LAUNCH(L.timer, (kb_gateup<512, 14>), g512, dim3(kBlk), 0, s, L);
   else if (L.H == 8192)
-    hipLaunchKernelGGL((kb_gateup<512, 16>), g512, dim3(kBlk), 0, s, L);
+    MOE_LAUNCH(L.timer, (kb_gateup<512, 16>), g512, dim3(kBlk), 0, s, L);
   else if (L.H % 512 == 0)
-    hipLaunchKernelGGL((kb_gateup<512, 0>), g512, dim3(kBlk), 0, s, L);
+    MOE_LAUNCH(L.timer, (kb_gateup<512, 0>), g512, dim3(kBlk), 0, s, L);
   else
-    hipLaunchKernelGGL((kb_gateup<256, 0>), dim3(kNumCUs * kGroupedBlocksPerCU), dim3(kBlk), 0, s, L);
+    MOE_LAUNCH(L.timer, (kb_gateup<256, 0>), dim3(kNumCUs * kGroupedBlocksPerCU), dim3(kBlk), 0, s, L);
   return hipPeekAtLastError();
 }
 
 hipError_t launch_down_tb(const LayerTB& L, hipStream_t s) {
   const dim3 grid(kNumCUs * kDownBlocksPerCU);
   if (L.F == 2048)
-    hipLaunchKernelGGL((kb_down_flat<512, 4>), grid, dim3(kDnBlock), 0, s, L);
+    MOE_LAUNCH(L.timer, (kb_down_flat<512, 4>), grid, dim3(kDnBlock), 0, s, L);
   else if (L.F % 512 == 0)
-    hipLaunchKernelGGL(kb_down<512>, grid, dim3(kDnBlock), 0, s, L);
+    MOE_LAUNCH(L.timer, kb_down<512>, grid, dim3(kDnBlock), 0, s, L);
   else if (L.F % 256 == 0)
-    hipLaunchKernelGGL(kb_down<256>, grid, dim3(kDnBlock), 0, s, L);
+    MOE_LAUNCH(L.timer, kb_down<256>, grid, dim3(kDnBlock), 0, s, L);
   else
-    hipLaunchKernelGGL(kb_down<128>, grid, dim3(kDnBlock), 0, s, L);
+    MOE_LAUNCH(L.timer, kb_down<128>, grid, dim3(kDnBlock), 0, s, L);
   return hipPeekAtLastError();
 }
 
 hipError_t launch_combine_tb(const LayerTB& L, hipStream_t s) {
   const int chunks = (L.H + 8 * kBlk - 1) / (8 * kBlk);
-  hipLaunchKernelGGL(kb_combine, dim3(L.T, chunks), dim3(kBlk), 0, s, L);
+  MOE_LAUNCH(L.timer, kb_combine, dim3(L.T, chunks), dim3(kBlk), 0, s, L);
   return hipPeekAtLastError();
 }
 

@@ -1,9 +1,44 @@
 // Internal launch interface between the C ABI (abi.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+namespace moe {
+
+// Optional per-kernel timing for the measurement entry point: the i-th
+// kernel a call launches records start[i] when it starts executing and
+// stop[i] when it ends (hipExtLaunchKernel); kernels past n launch plainly.
+struct KernelTimer {
+  hipEvent_t* start;
+  hipEvent_t* stop;
+  int n;     // event pairs available
+  int used;  // kernels launched so far
+};
+
+inline bool timer_slot(KernelTimer* tm, hipEvent_t* a, hipEvent_t* b) {
+  if (!tm) return false;
+  const int i = tm->used++;
+  if (i >= tm->n) return false;
+  *a = tm->start[i];
+  *b = tm->stop[i];
+  return true;
+}
+
+}  // namespace moe
+
+// Launch K (parenthesised when it has template arguments) plainly, or with
+// the timer's next event pair.
+#define MOE_LAUNCH(TM, K, G, B, LDS, S, ...)                                    \
+  do {                                                                          \
+    hipEvent_t moe_e0_ = nullptr, moe_e1_ = nullptr;                            \
+    if (::moe::timer_slot((TM), &moe_e0_, &moe_e1_))                             \
+      hipExtLaunchKernelGGL(K, G, B, LDS, S, moe_e0_, moe_e1_, 0u, __VA_ARGS__); \
+    else                                                                        \
+      hipLaunchKernelGGL(K, G, B, LDS, S, __VA_ARGS__);                          \
+  } while (0)
 
 namespace moe {
 
@@ -55,6 +90,7 @@ struct LayerT1 {
   float* logits_out;
   int32_t* idx_out;
   float* w_out;
+  KernelTimer* timer;  // host-side, measurement entry point only (else null)
 };
 
 // K1a router, K2 top-k when idx is null and gate/up (shared expert first
@@ -66,6 +102,9 @@ hipError_t launch_topk_t1(const LayerT1& L, hipStream_t s);
 hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* idx,
                             float* act, bool with_shared, hipStream_t s);
 hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s);
+// The whole single-token layer: router, gate/up with the selection, down +
+// combine.
+hipError_t launch_layer_t1(LayerT1& L, hipStream_t s);
 
 // ---- 2 <= T <= 64 path ------------------------------------------------------
 
@@ -100,6 +139,7 @@ struct LayerTB {
   float* w_out;               // [T][k]
   int32_t* offsets_out;       // [E + 1] grouping offsets
   int32_t* pairs_out;         // [T k] pair ids sorted by expert
+  KernelTimer* timer;         // host-side, measurement entry point only (else null)
 };
 
 // Router K splits for hidden size H: the largest KS <= 16 with H % (128 KS) == 0.
@@ -119,5 +159,6 @@ hipError_t launch_rmsnorm_tb(const uint16_t* h, const uint16_t* gamma, float eps
                              uint16_t* xn, hipStream_t s);
 
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace moe

@@ -43,6 +43,7 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / kWave;
+constexpr int kK3SlabW = 8;  // waves per workgroup of the slab down kernel (two per SIMD)
 constexpr int kMaxH = 8192;
 constexpr int kMaxChunks = kMaxH / 8;          // 16-byte chunks of a bf16 row
 constexpr int kChunksPerLane = kMaxChunks / kBlock;
@@ -587,12 +588,12 @@ __global__ __launch_bounds__(kBlock, kK2WavesPerSimd) void k2_gateup(LayerT1 L, 
 //
 // The combine crosses workgroups: the nslots workgroups of a chunk store
 // their weighted rows with agent-scope atomic stores (coherent across the
-// L2s), wait until the stores have completed and then count themselves on
-// the chunk's counter.  The workgroup that counts last reads every slot's
-// rows with agent-scope atomic loads, sums them in slot order
-// (deterministic: no floating-point atomics), adds the residual, stores bf16
-// and clears the counter for the next call.  Only these coherent accesses
-// cross workgroups, so no cache writeback or invalidate is needed.
+// L2s) and then count themselves on the chunk's counter with one
+// acquire-release increment per workgroup, which orders the rows before the
+// count.  The workgroup that counts last (its increment acquires every
+// earlier one) reads every slot's rows with agent-scope atomic loads, sums
+// them in slot order (deterministic: no floating-point atomics), adds the
+// residual, stores bf16 and clears the counter for the next call.
 constexpr int kK3W = 8;                       // waves per workgroup (two per SIMD)
 // row groups in flight per wave, within 256 registers (two waves per SIMD)
 constexpr int k3_depth(int ni) { return ni == 4 ? 4 : 6; }
@@ -766,10 +767,16 @@ __global__ __launch_bounds__(W * kWave) void k3_down(LayerT1 L, int nchunk,
     for (int kk = 0; kk < kqn; ++kk) v += red[kk * crows + r];
     st_agent(part + r, w * v);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the stores have completed
+  // Every wave's stores happen before thread 0's increment (barrier); the
+  // increment releases them at agent scope and, in the last workgroup,
+  // acquires the other workgroups' rows, which the barrier then hands on
+  // to every thread of the workgroup.  Each wave also waits for its own
+  // stores before the barrier, so they have reached the coherent level
+  // whatever order the memory path keeps between waves.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(&L.counters[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    last = __hip_atomic_fetch_add(&L.counters[c], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
            (uint32_t)(nslots - 1);
   __syncthreads();
   if (!last) return;
@@ -801,7 +808,6 @@ __global__ __launch_bounds__(W * kWave) void k3_down(LayerT1 L, int nchunk,
 // (slot, row group) pairs in slot-major order, so it reads its B operand
 // from LDS only when its slot changes.  The weighted row sums of every slot
 // meet in LDS and are added in slot order, with the residual.
-constexpr int kK3SlabW = 8;                  // waves per workgroup (two per SIMD)
 constexpr int kK3SlabD = 4;                  // row groups in flight per wave
 constexpr size_t kK3SlabLds = 156 * 1024;    // LDS budget: activations + row sums
 
@@ -957,7 +963,7 @@ template <int B>
 hipError_t k2_launch(const LayerT1& L, const uint16_t* x, const int32_t* idx, float* act,
                      int n_gu, int lanes, int ns, bool pre, hipStream_t s) {
 #define K2(LN, P) \
-  hipLaunchKernelGGL((k2_gateup<B, LN, P>), dim3(n_gu), dim3(kBlock), 0, s, L, x, idx, act, lanes, ns)
+  MOE_LAUNCH(L.timer, (k2_gateup<B, LN, P>), dim3(n_gu), dim3(kBlock), 0, s, L, x, idx, act, lanes, ns)
   if (lanes == 32) {  // the common case (H a multiple of 1024): offsets fold
     if (pre) K2(32, true);
     else K2(32, false);
@@ -976,19 +982,19 @@ hipError_t k3_slab_launch(const LayerT1& L, int gpb, int nblk, size_t lds, hipSt
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k3_slab<CPR, NI, SC1>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k3_slab<CPR, NI, SC1>), dim3(nblk), dim3(kK3SlabW * kWave), lds, s, L, gpb);
+  MOE_LAUNCH(L.timer, (k3_slab<CPR, NI, SC1>), dim3(nblk), dim3(kK3SlabW * kWave), lds, s, L, gpb);
   return hipPeekAtLastError();
 }
 
 }  // namespace
 
 hipError_t launch_router_t1(const LayerT1& L, hipStream_t s) {
-  hipLaunchKernelGGL(k1_router, dim3(ceil_div(L.E, kWaves)), dim3(kBlock), 0, s, L);
+  MOE_LAUNCH(L.timer, k1_router, dim3(ceil_div(L.E, kWaves)), dim3(kBlock), 0, s, L);
   return hipPeekAtLastError();
 }
 
 hipError_t launch_topk_t1(const LayerT1& L, hipStream_t s) {
-  hipLaunchKernelGGL(k1_topk, dim3(1), dim3(kBlock), 0, s, L);
+  MOE_LAUNCH(L.timer, k1_topk, dim3(1), dim3(kBlock), 0, s, L);
   return hipPeekAtLastError();
 }
 
@@ -1021,18 +1027,32 @@ hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s) {
+namespace {
+
+// How the down projection + combine runs for a layer's shape.
+struct DownPlan {
+  bool ok, slab;
+  int cpr, ni, ni1, nb;
+  int gpb, nblk;       // slab kernel: row groups per workgroup, workgroups
+  size_t lds;          // slab kernel: dynamic LDS bytes
+  int kqn, nsn, nchunk;  // split kernel
+};
+
+DownPlan plan_down(const LayerT1& L) {
+  DownPlan P{};
   const int nslots = L.k + (L.S ? 1 : 0);
   const int nb = L.F / 32;
-  if (L.F % 128 || L.H % 64 || nslots < 1) return hipErrorInvalidValue;
+  P.nb = nb;
+  if (L.F % 128 || L.H % 64 || nslots < 1) return P;
   // one expert's down matrix is addressed through 32-bit buffer offsets
-  if ((size_t)L.H * (size_t)(L.F / 2) > 0x7FFFFFFFu) return hipErrorInvalidValue;
+  if ((size_t)L.H * (size_t)(L.F / 2) > 0x7FFFFFFFu) return P;
   const int cpr = nb <= 4 ? 4 : (nb <= 8 ? 8 : 16);  // blocks per row per instruction
   const int ninst = ceil_div(nb, cpr);               // instructions per row
-  const int ni = ninst >= 4 ? 4 : (ninst >= 2 ? 2 : 1);
-  const int kqn = ceil_div(ninst, ni);
+  P.cpr = cpr;
+  P.ni = ninst >= 4 ? 4 : (ninst >= 2 ? 2 : 1);
+  P.kqn = ceil_div(ninst, P.ni);
   {  // every slot in one workgroup when the activations fit in LDS
-    const int ni1 = ninst <= 1 ? 1 : (ninst <= 2 ? 2 : 4);
+    P.ni1 = ninst <= 1 ? 1 : (ninst <= 2 ? 2 : 4);
     const int rpi = 64 / cpr, nrg = L.H / rpi;
     int gpb = ceil_div(nrg, kNumCU);  // about one workgroup per CU
     // narrow experts: when a one-group slab needs little LDS, several
@@ -1040,39 +1060,70 @@ hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s) {
     // workgroups instead of 224, 18.8 -> 18.5 us per layer)
     if (1024 * (size_t)ceil_div(4L * nslots * L.F, 1024) + 4 * (size_t)nslots * rpi <= 40 * 1024)
       gpb = ceil_div(nrg, 2 * kNumCU);
-    const int nblk = ceil_div(nrg, gpb);
-    const size_t lds = 1024 * (size_t)ceil_div(4L * nslots * L.F, 1024) + 4 * (size_t)nslots * gpb * rpi;
-    if (ninst <= 4 && lds <= kK3SlabLds) {
-      if (cpr == 4) return k3_slab_launch<4, 1>(L, gpb, nblk, lds, s);
-      if (cpr == 8) return k3_slab_launch<8, 1>(L, gpb, nblk, lds, s);
-      if (ni1 == 1) return k3_slab_launch<16, 1>(L, gpb, nblk, lds, s);
-      if (ni1 == 2)
-        return nb == 32 ? k3_slab_launch<16, 2, true>(L, gpb, nblk, lds, s)
-                        : k3_slab_launch<16, 2>(L, gpb, nblk, lds, s);
-      return nb == 64 ? k3_slab_launch<16, 4, true>(L, gpb, nblk, lds, s)
-                      : k3_slab_launch<16, 4>(L, gpb, nblk, lds, s);
+    P.gpb = gpb;
+    P.nblk = ceil_div(nrg, gpb);
+    P.lds = 1024 * (size_t)ceil_div(4L * nslots * L.F, 1024) + 4 * (size_t)nslots * gpb * rpi;
+    if (ninst <= 4 && P.lds <= kK3SlabLds) {
+      P.ok = P.slab = true;
+      return P;
     }
   }
-  const int maxw = kK3W;
-  if (kqn > maxw) return hipErrorInvalidValue;
-  const int nsn = maxw / kqn;
+  if (P.kqn > kK3W) return P;
+  P.nsn = kK3W / P.kqn;
   const int rpi = 64 / cpr, nrg = L.H / rpi;
   // about one workgroup per CU, within the counters and the LDS slice sums
   int nchunk = kNumCU / nslots;
   if (nchunk < 1) nchunk = 1;
   const int cap = nrg < kK3MaxChunks ? nrg : kK3MaxChunks;
   if (nchunk > cap) nchunk = cap;
-  while (kqn * ceil_div(nrg, nchunk) * rpi > kK3RedFloats && nchunk < cap) ++nchunk;
-  if (kqn * ceil_div(nrg, nchunk) * rpi > kK3RedFloats) return hipErrorInvalidValue;
+  while (P.kqn * ceil_div(nrg, nchunk) * rpi > kK3RedFloats && nchunk < cap) ++nchunk;
+  if (P.kqn * ceil_div(nrg, nchunk) * rpi > kK3RedFloats) return P;
+  P.nchunk = nchunk;
+  P.ok = true;
+  return P;
+}
+
+hipError_t launch_down(const LayerT1& L, const DownPlan& P, hipStream_t s) {
+  if (!P.ok) return hipErrorInvalidValue;
+  if (P.slab) {
+    const int gpb = P.gpb, nblk = P.nblk;
+    const size_t lds = P.lds;
+    if (P.cpr == 4) return k3_slab_launch<4, 1>(L, gpb, nblk, lds, s);
+    if (P.cpr == 8) return k3_slab_launch<8, 1>(L, gpb, nblk, lds, s);
+    if (P.ni1 == 1) return k3_slab_launch<16, 1>(L, gpb, nblk, lds, s);
+    if (P.ni1 == 2)
+      return P.nb == 32 ? k3_slab_launch<16, 2, true>(L, gpb, nblk, lds, s)
+                        : k3_slab_launch<16, 2>(L, gpb, nblk, lds, s);
+    return P.nb == 64 ? k3_slab_launch<16, 4, true>(L, gpb, nblk, lds, s)
+                      : k3_slab_launch<16, 4>(L, gpb, nblk, lds, s);
+  }
+  const int nslots = L.k + (L.S ? 1 : 0);
+  const int nchunk = P.nchunk, kqn = P.kqn, nsn = P.nsn;
   const dim3 g(nslots * nchunk), b(kqn * nsn * kWave);
-#define K3(C, N) hipLaunchKernelGGL((k3_down<C, N, k3_depth(N), kK3W>), g, b, 0, s, L, nchunk, kqn, nsn)
-  if (cpr == 4) K3(4, 1);
-  else if (cpr == 8) K3(8, 1);
-  else if (ni == 1) K3(16, 1);
-  else if (ni == 2) K3(16, 2);
+#define K3(C, N) MOE_LAUNCH(L.timer, (k3_down<C, N, k3_depth(N), kK3W>), g, b, 0, s, L, nchunk, kqn, nsn)
+  if (P.cpr == 4) K3(4, 1);
+  else if (P.cpr == 8) K3(8, 1);
+  else if (P.ni == 1) K3(16, 1);
+  else if (P.ni == 2) K3(16, 2);
   else K3(16, 4);
 #undef K3
   return hipPeekAtLastError();
+}
+
+}  // namespace
+
+hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s) {
+  return launch_down(L, plan_down(L), s);
+}
+
+hipError_t launch_layer_t1(LayerT1& L, hipStream_t s) {
+  const DownPlan P = plan_down(L);
+  if (!P.ok) return hipErrorInvalidValue;
+  hipError_t e = launch_router_t1(L, s);
+  if (e != hipSuccess) return e;
+  e = launch_gateup_t1(L, L.gamma ? L.xn : L.x, nullptr, nullptr, true, s);
+  if (e != hipSuccess) return e;
+  return launch_down(L, P, s);
 }
 
 // ------------------------------------------------------------------ utils
@@ -1082,6 +1133,46 @@ __global__ void zero_fill_kernel(uint32_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
 }
 }  // namespace
+
+namespace {
+// Plain streaming read of a buffer: every thread keeps kStreamUnroll
+// 16-byte nontemporal loads in flight, a wave's loads of one round cover
+// 1 KB of contiguous bytes, and each workgroup stores one xor of what it
+// read (so that no load is dead).
+constexpr int kStreamUnroll = 8;
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, size_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  __shared__ uint32_t red[4];
+  const size_t stride = (size_t)gridDim.x * 256 * kStreamUnroll;
+  uint32_t acc = 0;
+  for (size_t base = (size_t)blockIdx.x * 256 * kStreamUnroll + threadIdx.x; base < n16; base += stride) {
+    uint4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const size_t i = base + (size_t)u * 256;
+      v[u] = ld_stream16(reinterpret_cast<const uint8_t*>(p + (i < n16 ? i : n16 - 1)));
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off, kWave);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+}  // namespace
+
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const size_t per = (size_t)256 * kStreamUnroll;
+  const size_t want = (n16 + per - 1) / per;
+  const unsigned g = (unsigned)(want < MOE_STREAM_SINK_WORDS ? want : MOE_STREAM_SINK_WORDS);
+  hipLaunchKernelGGL(stream_read_kernel, dim3(g), dim3(256), 0, s, reinterpret_cast<const uint4*>(p),
+                     n16, sink);
+  return hipPeekAtLastError();
+}
 
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
   const size_t n = bytes / 4;

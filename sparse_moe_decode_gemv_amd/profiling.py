@@ -173,6 +173,23 @@ def counters(fetch_csv: str, write_csv: str) -> str:
     return "\n".join(out)
 
 
+def read_counter_summary(path: str):
+    """(header values, HBM bytes per launch by kernel) of a summary written by
+    ``counters``: the ``name: value`` lines and the table rows."""
+    vals, table = {}, {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            cols = re.split(r"\s{2,}", line.strip())
+            if len(cols) == 5 and cols[-1].isdigit():
+                table[cols[0]] = int(cols[-1])
+            elif ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    return vals, table
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "trace":
         print(trace(argv[1]))

@@ -18,7 +18,8 @@ def k3():
 def test_library_exports_every_declared_function():
     names = M.header_functions()
     assert {"moe_router_topk", "moe_decode_layer", "moe_decode_stack",
-            "moe_workspace_size", "moe_expert_gateup", "moe_group_by_expert"} <= set(names)
+            "moe_workspace_size", "moe_expert_gateup", "moe_group_by_expert",
+            "moe_decode_layer_timed", "moe_stream_read"} <= set(names)
     L = M.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -118,3 +119,29 @@ def test_router_and_stack_argument_errors():
 def test_python_binding_raises_on_error():
     with pytest.raises(M.MoeError):
         M.workspace_size(M.make_shape(7000, 896, 16, 2048, 1, 2048), 1)
+
+
+def test_measurement_entry_points_validate_on_the_host():
+    """The timed layer and the streaming read reject bad arguments before
+    anything is enqueued (no GPU needed)."""
+    import ctypes
+    L = M.lib()
+    s = k3()
+    w = M.MoeLayerWeights()
+    ev = (ctypes.c_void_p * 16)(*([FAKE] * 16))
+    nk = ctypes.c_int32(-1)
+    args = (ctypes.byref(s), ctypes.byref(w), FAKE, FAKE, FAKE + (1 << 20), 1, None, None, FAKE,
+            1 << 26, None)
+    assert L.moe_decode_layer_timed(*args, None, 3, ctypes.byref(nk)) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_decode_layer_timed(*args, ev, M.MOE_MAX_LAYER_KERNELS + 1,
+                                    ctypes.byref(nk)) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_decode_layer_timed(*args, ev, 3, None) == M.MOE_ERR_INVALID_ARG
+    zero = (ctypes.c_void_p * 2)(FAKE, None)
+    assert L.moe_decode_layer_timed(*args, zero, 1, ctypes.byref(nk)) == M.MOE_ERR_INVALID_ARG
+    # weights missing: the layer's own validation still runs first
+    assert L.moe_decode_layer_timed(*args, ev, 3, ctypes.byref(nk)) == M.MOE_ERR_INVALID_ARG
+    assert nk.value in (-1, 0)
+    assert L.moe_stream_read(None, 1024, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_stream_read(FAKE, 1000, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_stream_read(FAKE + 8, 1024, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_stream_read(FAKE, 1024, None, None) == M.MOE_ERR_INVALID_ARG

@@ -33,12 +33,15 @@ SMALL = {
 
 
 def run_layer(w, dl, x_bits, residual="x", want_logits=False):
+    return run_layer_ws(w, dl, x_bits, workspace(w, 1), residual)
+
+
+def run_layer_ws(w, dl, x_bits, ws, residual="x"):
     t = torch()
     x = dev_u16(x_bits.reshape(1, -1))
     out = t.empty_like(x)
     idx = t.empty((1, w.k), dtype=t.int32, device="cuda")
     wts = t.empty((1, w.k), dtype=t.float32, device="cuda")
-    ws = workspace(w, 1)
     res = x if residual == "x" else residual
     M.decode_layer(shape_of(w), weights_of(dl), x, res, out, 1, idx, wts, ws)
     t.cuda.synchronize()
@@ -274,13 +277,40 @@ def test_deterministic_and_poison_proof():
 M_COUNTER = 256  # MOE_WS_COUNTER_BYTES
 
 
-@pytest.mark.parametrize("name", ["tiny", "k3_batch1"])
+@pytest.mark.parametrize("name", ["wide_f", "f8192"])
+def test_cross_workgroup_combine_deterministic_and_poison_proof(name):
+    """FFN 4096 and 8192 take the down kernel whose row chunks are combined
+    across workgroups (counter per chunk).  Repeated calls with the scratch
+    part of the workspace poisoned before each give identical bits, match
+    the oracle, and leave the counters at zero."""
+    t = torch()
+    w = SMALL[name]
+    dl = device_layer(w, 0)
+    (d, x), = pick_tokens(w, dl.router_host, 1, start=20)
+    xd = dev_u16(x.reshape(1, -1))
+    ws = workspace(w, 1)
+    outs = []
+    for poison in (False, True, True):
+        out = t.full_like(xd, 0x7FC0 if poison else 0)
+        if poison:
+            ws[M_COUNTER:].fill_(0xFF)
+        M.decode_layer(shape_of(w), weights_of(dl), xd, xd, out, 1, None, None, ws)
+        t.cuda.synchronize()
+        outs.append(host_u16(out).copy())
+        assert not ws[:M_COUNTER].any().item(), "counters not left at zero"
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    ref = oracle_layer(w, 0, dl.router_host, x, x)
+    assert max_err_ratio(outs[0], ref["out"])[0] <= TOL
+
+
+@pytest.mark.parametrize("name", ["tiny", "k3_batch1", "wide_f"])
 def test_graph_replay_matches_eager(name):
     """One layer captured in a HIP graph, replayed with new inputs copied in
     between; every replay equals the eager call on the same input, and the
-    workspace's counter head is left at zero."""
+    workspace's counter head is left at zero (wide_f: the down rows are
+    combined across workgroups through those counters)."""
     t = torch()
-    w = G.WORKLOADS[name]
+    w = SMALL[name] if name in SMALL else G.WORKLOADS[name]
     dl = device_layer(w, 0)
     toks = [x for _, x in pick_tokens(w, dl.router_host, 4, start=200)]
     ws = workspace(w, 1)

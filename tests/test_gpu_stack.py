@@ -4,14 +4,18 @@ hidden state between layers) against the fp64 oracle.
 Teacher-forced: oracle layer l is fed the GPU's own bf16 h_l, so every layer
 is checked on identical inputs against the per-layer bar (max-abs-error <=
 2e-2 * rms) and, element by element, against the correctly rounded oracle
-value.  End to end: the oracle chain from h_0 is compared with the GPU chain;
-the activation draw (tests/golden/stack8_token.json, written by
+value: at most a FLIP_RATE share of the elements may round to the other
+neighbour, each by at most one ulp of the layer's largest element.
+
+End to end: the oracle chain from h_0 is compared with the GPU chain; the
+activation draw (tests/golden/stack8_token.json, written by
 make_stack_token.py from the oracle alone) has a top-k gap of at least 1e-2
 at every layer of the oracle chain, so the selected sets must agree at every
-layer.  The two bf16 chains drift apart by rounding alone (one ulp flipped in
-1% of one layer's outputs moves the oracle's own chain by ~4e-2 * rms after
-seven more layers), so the final output is held to the per-layer bar summed
-over the layers, L * 2e-2 * rms.
+layer.  The final error is the last layer's own (held to 2e-2 above) plus the
+drift the earlier layers' rounding flips cause.  make_stack_drift.py measures
+that drift with the oracle alone, over 64 chains flipped at FLIP_RATE after
+every layer (tests/golden/stack8_drift.json), so the end-to-end bound is
+2e-2 + drift_max.
 """
 import json
 import os
@@ -24,12 +28,18 @@ from gpu_helpers import (TOL, G, M, O, check_topk, dev_u16, host_u16, max_err_ra
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-# Share of a layer's bf16 outputs allowed to differ from the oracle's fp64
-# output rounded to nearest even: fp32 accumulation leaves the pre-rounding
-# value within ~1e-5 of the summands' scale, so only values that close to a
-# rounding boundary round the other way (by one ulp, or by a few ulps where
-# the residual and the MoE output cancel and the result is small).
-MAX_FLIPS = 0.02
+
+
+def drift_fixture():
+    """The oracle-only drift bound (make_stack_drift.py).  Its flip rate is
+    the share of a layer's bf16 outputs allowed to differ from the oracle's
+    fp64 output rounded to nearest even: fp32 accumulation leaves the
+    pre-rounding value within ~1e-5 of the summands' scale, so only values
+    that close to a rounding boundary round the other way (by one ulp, or by
+    a few ulps of a small value where the residual and the MoE output
+    cancel)."""
+    with open(os.path.join(GOLDEN, "stack8_drift.json")) as f:
+        return json.load(f)
 
 
 def _order(b):
@@ -39,14 +49,21 @@ def _order(b):
 
 def bf16_mismatch(gpu_bits, ref_out):
     """(share of elements where the GPU's bf16 differs from the correctly
-    rounded oracle value, largest distance in ulps)."""
+    rounded oracle value, largest distance in ulps, largest absolute
+    difference in ulps of the largest element)."""
     want = O.f64_to_bf16(ref_out)
-    d = np.abs(_order(np.asarray(gpu_bits, np.uint16)) - _order(want))
-    return float((d != 0).mean()), int(d.max())
+    gb = np.asarray(gpu_bits, np.uint16)
+    d = np.abs(_order(gb) - _order(want))
+    top = np.abs(O.bf16_to_f64(want)).max()
+    ulp_top = 2.0 ** (np.floor(np.log2(top)) - 7)
+    absd = np.abs(O.bf16_to_f64(gb) - O.bf16_to_f64(want)).max() / ulp_top
+    return float((d != 0).mean()), int(d.max()), float(absd)
 
 
 def test_stack8_teacher_forced_and_end_to_end():
     t = torch()
+    drift = drift_fixture()
+    max_flips = drift["flip_rate"]
     release_device_layers()
     w = G.WORKLOADS["k3_stack8"]
     with open(os.path.join(GOLDEN, "stack8_token.json")) as f:
@@ -71,14 +88,19 @@ def test_stack8_teacher_forced_and_end_to_end():
     # teacher forced: layer l on the GPU's h_l
     teacher = [x.reshape(1, -1)] + [tr[l] for l in range(w.L - 1)]
     recs = O.moe_stack(x, ol, w.eps, teacher=teacher, pmap=pmap)
+    stats = []
     for l, r in enumerate(recs):
         n = check_topk(gi[l], r, w.k)
         err = max_err_ratio(tr[l], r["out"])[0]
-        flips, worst = bf16_mismatch(tr[l][0], r["out"][0])
+        flips, worst, absd = bf16_mismatch(tr[l][0], r["out"][0])
         print(f"layer {l}: topk checked={n} max_err/rms={err:.3e} "
-              f"bf16 != rounded oracle: {flips:.4f} of elements, max {worst} ulp")
+              f"bf16 != rounded oracle: {flips:.5f} of elements, max {worst} ulp "
+              f"({absd:.2f} ulp of the largest element)")
+        stats.append((l, err, flips, absd))
+    for l, err, flips, absd in stats:
         assert err <= TOL, (l, err)
-        assert flips <= MAX_FLIPS, (l, flips, worst)
+        assert flips <= max_flips, (l, flips)
+        assert absd <= 1.0, (l, absd)
     # end to end: the oracle's own chain.  Its hidden states drift from the
     # GPU's by bf16 ulps layer after layer, so only the selected sets (k-th to
     # (k+1)-th gap >= 1e-2 at every layer for this draw) are compared; the
@@ -87,7 +109,9 @@ def test_stack8_teacher_forced_and_end_to_end():
     for l, r in enumerate(chain):
         assert check_topk(gi[l], r, w.k, ordered=False, gap=1e-2) == 1, l
     err = max_err_ratio(tr[-1], chain[-1]["out"])[0]
-    print(f"end to end: max_err/rms={err:.3e} (bound {w.L * TOL:.2f})")
-    assert err <= w.L * TOL
+    bound = TOL + drift["drift_max"]
+    print(f"end to end: max_err/rms={err:.3e} (bound {bound:.3e} = {TOL} + drift "
+          f"{drift['drift_max']:.3e})")
+    assert err <= bound
     del layers
     release_device_layers()
