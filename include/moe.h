@@ -68,6 +68,7 @@ extern "C" {
 #define MOE_WS_COUNTER_BYTES 256
 #define MOE_MAX_LAYER_KERNELS 8    /* kernels one moe_decode_layer call launches, at most */
 #define MOE_STREAM_SINK_WORDS 4096 /* uint32 words moe_stream_read may write to `sink` */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20) /* scratch of moe_decode_layer_noalloc, per GPU */
 
 typedef enum {
   MOE_OK = 0,
@@ -145,6 +146,25 @@ int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const u
                      const uint16_t* residual, uint16_t* out, int32_t n_tokens,
                      int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* moe_decode_layer for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same validation, kernels and results, with no workspace argument.
+ * Its scratch is a library-owned device array of MOE_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) per GPU, held until the process ends; nothing is allocated or
+ * freed by any call.  Shapes whose workspace (moe_workspace_size for
+ * n_tokens) exceeds that size return MOE_ERR_UNSUPPORTED: every
+ * single-token shape fits, and the K3-sized layer fits up to about 23
+ * tokens.  Every call on a GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (different streams, or host threads) race and give
+ * undefined results; serialise them.  The first call on each device looks
+ * up the array's address and clears its counter head with a fill kernel on
+ * `stream`; make that first call outside graph capture (later calls may be
+ * captured).  Other arguments as for moe_decode_layer. */
+int moe_decode_layer_noalloc(const moe_shape* shape, const moe_layer_weights* w,
+                             const uint16_t* x, const uint16_t* residual, uint16_t* out,
+                             int32_t n_tokens, int32_t* topk_idx_out, float* topk_w_out,
+                             void* stream);
 
 /* Measurement variant of moe_decode_layer: the same validation, kernels and
  * results, but kernel i of the call is launched with hipExtLaunchKernel so

@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_MAX_LAYER_KERNELS = 8
 MOE_STREAM_SINK_WORDS = 4096
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class MoeError(RuntimeError):
@@ -65,6 +66,8 @@ _SIG = {
                                 ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
                                 ctypes.POINTER(ctypes.c_int32)]),
     "moe_stream_read": ([_P, ctypes.c_size_t, _P, _P]),
+    "moe_decode_layer_noalloc": ([ctypes.POINTER(MoeShape), ctypes.POINTER(MoeLayerWeights), _P,
+                                  _P, _P, ctypes.c_int32, _P, _P, _P]),
 }
 
 
@@ -185,6 +188,13 @@ def decode_layer_timed(shape, weights, x, residual, out, n_tokens, topk_idx_out,
         _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream), handles, n, ctypes.byref(nk)))
     return nk.value
+
+
+def decode_layer_noalloc(shape, weights, x, residual, out, n_tokens, topk_idx_out, topk_w_out,
+                         stream=None):
+    _check("moe_decode_layer_noalloc", lib().moe_decode_layer_noalloc(
+        ctypes.byref(shape), ctypes.byref(weights), _ptr(x), _ptr(residual), _ptr(out), n_tokens,
+        _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream)))
 
 
 def stream_read(buf, sink, stream=None):

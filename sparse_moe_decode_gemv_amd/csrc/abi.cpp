@@ -5,7 +5,15 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
+
+// Scratch of moe_decode_layer_noalloc: one array per GPU, held until the
+// process ends.  Host code never uses its name as an address (on the host
+// it only stands for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -376,6 +384,47 @@ int moe_decode_layer_timed(const moe_shape* shape, const moe_layer_weights* w, c
                               ws_bytes, stream, &tm);
   if (rc == MOE_OK) *n_kernels = tm.used;
   return rc;
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` per device, once resolved
+
+// The current device's scratch address; on the first call for a device it is
+// looked up and the counter head is cleared by a fill kernel on `st`.
+int scratch_of_current_device(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    if (moe::launch_zero_fill(p, MOE_WS_COUNTER_BYTES, st) != hipSuccess) return MOE_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_decode_layer_noalloc(const moe_shape* shape, const moe_layer_weights* w, const uint16_t* x,
+                             const uint16_t* residual, uint16_t* out, int32_t n_tokens,
+                             int32_t* topk_idx_out, float* topk_w_out, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
+  if (n_tokens == 0) return MOE_OK;
+  if (ws_needed(*shape, n_tokens) > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device((hipStream_t)stream, &ws))) return rc;
+  return decode_layer(shape, w, x, residual, out, n_tokens, topk_idx_out, topk_w_out, ws,
+                      (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

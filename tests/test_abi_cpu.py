@@ -19,7 +19,8 @@ def test_library_exports_every_declared_function():
     names = M.header_functions()
     assert {"moe_router_topk", "moe_decode_layer", "moe_decode_stack",
             "moe_workspace_size", "moe_expert_gateup", "moe_group_by_expert",
-            "moe_decode_layer_timed", "moe_stream_read"} <= set(names)
+            "moe_decode_layer_timed", "moe_stream_read",
+            "moe_decode_layer_noalloc"} <= set(names)
     L = M.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -145,3 +146,23 @@ def test_measurement_entry_points_validate_on_the_host():
     assert L.moe_stream_read(FAKE, 1000, FAKE, None) == M.MOE_ERR_INVALID_ARG
     assert L.moe_stream_read(FAKE + 8, 1024, FAKE, None) == M.MOE_ERR_INVALID_ARG
     assert L.moe_stream_read(FAKE, 1024, None, None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_entry_rejects_shapes_beyond_its_scratch_on_the_host():
+    """A shape whose workspace exceeds the library's scratch array is refused
+    before any device call; one that fits only fails later on weights."""
+    import ctypes
+    L = M.lib()
+    s = k3()
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(s), 64, ctypes.byref(n)) == 0
+    assert n.value > M.MOE_NOALLOC_SCRATCH_BYTES
+    w = M.MoeLayerWeights()
+    assert L.moe_decode_layer_noalloc(ctypes.byref(s), ctypes.byref(w), FAKE, FAKE,
+                                      FAKE + (1 << 20), 64, None, None, None) == M.MOE_ERR_UNSUPPORTED
+    assert L.moe_decode_layer_noalloc(ctypes.byref(s), ctypes.byref(w), FAKE, FAKE,
+                                      FAKE + (1 << 20), 65, None, None, None) == M.MOE_ERR_UNSUPPORTED
+    assert L.moe_decode_layer_noalloc(None, ctypes.byref(w), FAKE, FAKE, FAKE, 1, None, None,
+                                      None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_decode_layer_noalloc(ctypes.byref(s), ctypes.byref(w), FAKE, FAKE, FAKE, 0, None,
+                                      None, None) == M.MOE_OK
