@@ -53,7 +53,9 @@
  *      (every multiple of 256 up to 2048, and e.g. 3072, 4096, 7168, 8192)
  *    F % 128 == 0, 128 <= F <= 8192
  *    1 <= k <= min(E, 32), 1 <= E <= 1024
- *    n_shared in {0, 1}; with a shared expert, shared_ffn == ffn
+ *    n_shared in {0, 1}; with a shared expert, shared_ffn % 128 == 0 and
+ *      128 <= shared_ffn <= 8192; shared_ffn != ffn only for calls of one
+ *      token (the grouped kernels of 2..64 tokens take one FFN width)
  */
 #ifndef MOE_DECODE_H
 #define MOE_DECODE_H
@@ -84,7 +86,7 @@ typedef struct {
   int32_t top_k;      /* k, routed experts used per token */
   int32_t ffn;        /* F, width of each routed expert */
   int32_t n_shared;   /* S in {0, 1} */
-  int32_t shared_ffn; /* Fs (== F when S = 1) */
+  int32_t shared_ffn; /* Fs, the shared expert's FFN width (when S = 1) */
 } moe_shape;
 
 typedef struct {

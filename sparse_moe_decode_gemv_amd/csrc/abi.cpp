@@ -33,20 +33,26 @@ struct Carver {
   }
 };
 
+// A shared expert whose FFN width differs from the routed experts'.
+bool shared_apart(const moe_shape& s) { return s.n_shared && s.shared_ffn != s.ffn; }
+
 // Single-token layout.
 struct WsT1 {
-  size_t reserved, logits, idx, wts, act_hl, part, xn, total;
+  size_t reserved, logits, idx, wts, act_hl, act_sh, part_sh, part, xn, total;
 };
 
 WsT1 ws_t1(const moe_shape& s) {
   WsT1 L{};
   Carver c;
   const size_t nslot = (size_t)s.top_k + (size_t)s.n_shared;
+  const bool apart = shared_apart(s);
   L.reserved = c.take(MOE_WS_COUNTER_BYTES);
   L.logits = c.take(sizeof(float) * s.n_experts);
   L.idx = c.take(sizeof(int32_t) * s.top_k);
   L.wts = c.take(sizeof(float) * s.top_k);
-  L.act_hl = c.take(sizeof(uint16_t) * 2 * nslot * s.ffn);
+  L.act_hl = c.take(sizeof(uint16_t) * 2 * (apart ? (size_t)s.top_k : nslot) * s.ffn);
+  L.act_sh = apart ? c.take(sizeof(uint16_t) * 2 * (size_t)s.shared_ffn) : 0;
+  L.part_sh = apart ? c.take(sizeof(float) * s.hidden) : 0;
   L.part = c.take(sizeof(float) * nslot * s.hidden);
   L.xn = c.take(sizeof(uint16_t) * s.hidden);
   L.total = c.o;
@@ -105,7 +111,8 @@ int check_shape(const moe_shape* s) {
     return MOE_ERR_INVALID_ARG;
   if (s->top_k > s->n_experts) return MOE_ERR_INVALID_ARG;
   if (s->n_shared > 1) return MOE_ERR_UNSUPPORTED;
-  if (s->n_shared == 1 && s->shared_ffn != s->ffn) return MOE_ERR_UNSUPPORTED;
+  if (s->n_shared == 1 && (s->shared_ffn <= 0 || s->shared_ffn % 128 || s->shared_ffn > moe::kMaxFfn))
+    return s->shared_ffn <= 0 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED;
   if (s->n_experts > moe::kMaxExperts || s->top_k > moe::kMaxTopK) return MOE_ERR_UNSUPPORTED;
   if (s->hidden % 256 || s->hidden > 8192) return MOE_ERR_UNSUPPORTED;
   if (moe::gateup_map(s->hidden).bpl > moe::kMaxBplGateUp) return MOE_ERR_UNSUPPORTED;
@@ -116,6 +123,14 @@ int check_shape(const moe_shape* s) {
 int check_tokens(int32_t T) {
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (T > moe::kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// The grouped (2..64 token) kernels take one FFN width for every group.
+int check_tokens_for(const moe_shape* s, int32_t T) {
+  int rc;
+  if ((rc = check_tokens(T))) return rc;
+  if (T > 1 && shared_apart(*s)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -178,8 +193,11 @@ LayerT1 make_layer(const moe_shape* s, const moe_layer_weights* w, void* ws) {
   L.k = s->top_k;
   L.F = s->ffn;
   L.S = s->n_shared;
+  L.Fs = s->n_shared ? s->shared_ffn : s->ffn;
   set_weights(L, s, w);
   L.logits = (float*)(b + W.logits);
+  L.act_sh = shared_apart(*s) ? (uint16_t*)(b + W.act_sh) : nullptr;
+  L.part_sh = shared_apart(*s) ? (float*)(b + W.part_sh) : nullptr;
   L.idx = (int32_t*)(b + W.idx);
   L.wts = (float*)(b + W.wts);
   L.act_hl = (uint16_t*)(b + W.act_hl);
@@ -253,7 +271,7 @@ const char* moe_status_string(int status) {
 
 int moe_workspace_size(const moe_shape* shape, int32_t max_tokens, size_t* bytes) {
   int rc;
-  if ((rc = check_shape(shape)) || (rc = check_tokens(max_tokens))) return rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens_for(shape, max_tokens))) return rc;
   if (!bytes) return MOE_ERR_INVALID_ARG;
   size_t n = ws_t1(*shape).total;
   if (max_tokens >= 2) {
@@ -322,7 +340,7 @@ int decode_layer(const moe_shape* shape, const moe_layer_weights* w, const uint1
                  int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
                  void* stream, moe::KernelTimer* timer) {
   int rc;
-  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens_for(shape, n_tokens))) return rc;
   if (n_tokens == 0) return MOE_OK;
   if ((rc = check_weights(shape, w, true))) return rc;
   if (!x || !aligned16(x) || !out || !aligned16(out)) return MOE_ERR_INVALID_ARG;
@@ -418,7 +436,7 @@ int moe_decode_layer_noalloc(const moe_shape* shape, const moe_layer_weights* w,
                              const uint16_t* residual, uint16_t* out, int32_t n_tokens,
                              int32_t* topk_idx_out, float* topk_w_out, void* stream) {
   int rc;
-  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens_for(shape, n_tokens))) return rc;
   if (n_tokens == 0) return MOE_OK;
   if (ws_needed(*shape, n_tokens) > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
   void* ws = nullptr;
@@ -437,7 +455,7 @@ int moe_decode_stack(const moe_shape* shape, const moe_layer_weights* layers,
                      int32_t n_tokens, int32_t* topk_idx_out, uint16_t* hidden_trace, void* ws,
                      size_t ws_bytes, void* stream) {
   int rc;
-  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens_for(shape, n_tokens))) return rc;
   if (n_layers < 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
   if (n_tokens == 0 || n_layers == 0) return MOE_OK;
   if (!layers || !gammas || !hidden || !aligned16(hidden)) return MOE_ERR_INVALID_ARG;

@@ -66,6 +66,7 @@ constexpr int kMaxTokens = 64;
 
 struct LayerT1 {
   int H, E, k, F, S;
+  int Fs;  // shared expert's FFN width (equal to F unless act_sh is set)
   // inputs
   const uint16_t* x;         // bf16 [H]: layer input, or h when gamma != null
   const uint16_t* gamma;     // RMSNorm gain (stack) or null
@@ -83,7 +84,14 @@ struct LayerT1 {
   float* wts;          // [k]
   uint16_t* act_hl;    // bf16 [2][k + S][F]: gated activations split as
                        // leading part + remainder (routed slots, then shared)
+  uint16_t* act_sh;    // shared expert of another width (Fs != F): its own
+                       // bf16 [2][Fs], and act_hl holds the k routed slots only
+  float* part_sh;      // [H]: the shared expert's down rows (Fs != F)
   float* part;         // [k + S][H]: weighted down-projection rows per slot
+  // down kernels' combine: add part_in[row] after the slots, or write the
+  // unrounded sum to part_out[row] instead of the output (Fs != F passes)
+  const float* part_in;
+  float* part_out;
   uint32_t* counters;  // per row chunk, zero between calls (workspace head)
   uint16_t* xn;        // [H] normalised input (stack)
   // optional user outputs

@@ -237,6 +237,8 @@ struct GateUpJob {
   float* act;            // fp32 [k + 1][F]: routed slots, then the shared expert
   uint16_t* act_hl;      // or bf16 [2][nslot][F]: leading parts, then remainders
   int nslot;
+  uint16_t* act_sh;      // shared expert of width Fs != F: bf16 [2][Fs] (else null)
+  int Fs;
 };
 
 // LANES > 0 fixes the lanes per row at compile time: the block offsets of a
@@ -363,10 +365,13 @@ struct GateUp {
       const uint16_t hi = f32_to_bf16(a);
       const float d = a - bf16_to_f32(hi);
       const uint16_t lo = f32_to_bf16(d == d ? d : 0.f);
-      const auto r = buf_rsrc(J.act_hl, 4u * (uint32_t)J.nslot * (uint32_t)J.F);
-      const uint32_t o = own ? 2u * (uint32_t)(slot * J.F + j) : 0xFFFFFFF0u;
+      // the shared expert has its own two planes when its width differs
+      const bool sep = sh && J.act_sh;  // wave-uniform
+      const uint32_t plane = sep ? (uint32_t)J.Fs : (uint32_t)J.nslot * (uint32_t)J.F;
+      const auto r = buf_rsrc(sep ? J.act_sh : J.act_hl, 4u * plane);
+      const uint32_t o = own ? 2u * (uint32_t)(sep ? j : slot * J.F + j) : 0xFFFFFFF0u;
       __builtin_amdgcn_raw_buffer_store_b16(hi, r, (int)o, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b16(lo, r, (int)(own ? o + 2u * (uint32_t)(J.nslot * J.F) : o), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(lo, r, (int)(own ? o + 2u * plane : o), 0, 0);
     } else {
       const auto r = buf_rsrc(J.act, 4u * (uint32_t)(J.k + 1) * (uint32_t)J.F);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r,
@@ -496,7 +501,7 @@ __device__ __forceinline__ void k2_body(const LayerT1& L, const uint16_t* __rest
   const GateUpJob J{L.g_codes,  L.g_scales,  L.u_codes,  L.u_scales, L.sg_codes, L.sg_scales,
                     L.su_codes, L.su_scales, e_lds,      L.H,        L.F,        L.k,
                     ns,         act,        act ? nullptr : L.act_hl,
-                    L.k + (L.S ? 1 : 0)};
+                    L.k + (L.S && !L.act_sh ? 1 : 0), act ? nullptr : L.act_sh, L.Fs};
   GateUp<BPLH, LANES> g;
   g.init(J, gu_lanes);
   const int first = blockIdx.x * kWaves + wid, ntask = ns + L.k * g.tps;
@@ -791,6 +796,11 @@ __global__ __launch_bounds__(W * kWave) void k3_down(LayerT1 L, int nchunk,
 #pragma unroll
     for (int u = 0; u <= kMaxTopK; ++u) tot += u < nslots ? pv[u] : 0.f;
     const int row = cg0 * RPI + r;
+    if (L.part_in) tot += L.part_in[row];
+    if (L.part_out) {
+      L.part_out[row] = tot;
+      continue;
+    }
     if (L.residual) tot += bf16_to_f32(L.residual[row]);
     const uint16_t o = f32_to_bf16(tot);
     L.out[row] = o;
@@ -941,11 +951,16 @@ __global__ __launch_bounds__(kK3SlabW * kWave) void k3_slab(LayerT1 L, int gpb) 
     if (i + k < n) use_group(i + k, ring[k]);
   __syncthreads();
 
-  // slots summed in order, residual added
+  // slots summed in order (then a separately computed shared expert), residual added
   for (int r = (int)threadIdx.x; r < srows; r += (int)blockDim.x) {
     float tot = 0.f;
     for (int q = 0; q < nslots; ++q) tot += red[q * srows + r];
     const int row = gb0 * RPI + r;
+    if (L.part_in) tot += L.part_in[row];
+    if (L.part_out) {
+      L.part_out[row] = tot;
+      continue;
+    }
     if (L.residual) tot += bf16_to_f32(L.residual[row]);
     const uint16_t o = f32_to_bf16(tot);
     L.out[row] = o;
@@ -1002,7 +1017,7 @@ hipError_t launch_gateup_t1(const LayerT1& L, const uint16_t* x, const int32_t* 
                             bool with_shared, hipStream_t s) {
   const RowMap gm = gateup_map(L.H);
   const int tps = L.F / (32 / gm.lanes);  // tasks per expert
-  const int ns = (with_shared && L.S) ? tps : 0;
+  const int ns = (with_shared && L.S) ? L.Fs / (32 / gm.lanes) : 0;  // the shared expert's
   const int tasks = ns + L.k * tps;
   const int cap = kNumCU * kK2WavesPerCU / kWaves;
   // about four tasks per wave where there are enough, else one per wave on
@@ -1117,6 +1132,32 @@ hipError_t launch_down_combine_t1(const LayerT1& L, hipStream_t s) {
 }
 
 hipError_t launch_layer_t1(LayerT1& L, hipStream_t s) {
+  if (L.S && L.act_sh) {
+    // shared expert of another width: its down projection is a pass of its
+    // own (one slot, FFN Fs) into part_sh, which the routed pass adds where
+    // the shared slot's rows would have been added (after the routed slots)
+    LayerT1 Ls = L;
+    Ls.k = 0;
+    Ls.F = L.Fs;
+    Ls.act_hl = L.act_sh;
+    Ls.act_sh = nullptr;
+    Ls.part_out = L.part_sh;
+    Ls.residual = nullptr;
+    Ls.out = nullptr;
+    Ls.trace = nullptr;
+    LayerT1 Lr = L;
+    Lr.S = 0;
+    Lr.part_in = L.part_sh;
+    const DownPlan Ps = plan_down(Ls), Pr = plan_down(Lr);
+    if (!Ps.ok || !Pr.ok) return hipErrorInvalidValue;
+    hipError_t e = launch_router_t1(L, s);
+    if (e != hipSuccess) return e;
+    e = launch_gateup_t1(L, L.gamma ? L.xn : L.x, nullptr, nullptr, true, s);
+    if (e != hipSuccess) return e;
+    e = launch_down(Ls, Ps, s);
+    if (e != hipSuccess) return e;
+    return launch_down(Lr, Pr, s);
+  }
   const DownPlan P = plan_down(L);
   if (!P.ok) return hipErrorInvalidValue;
   hipError_t e = launch_router_t1(L, s);

@@ -29,6 +29,13 @@ SMALL = {
     "f8192": G.Workload("f8192", T=1, H=256, E=4, k=2, F=8192, S=1, Fs=8192, seed=0x5EED010B),
     # the most experts and the largest top-k the library accepts together
     "emax": G.Workload("emax", T=1, H=512, E=1024, k=32, F=128, S=1, Fs=128, seed=0x5EED010C),
+    # a shared expert wider, and one narrower, than the routed experts
+    "fs_wide": G.Workload("fs_wide", T=1, H=1024, E=24, k=4, F=256, S=1, Fs=512, seed=0x5EED010D),
+    "fs_narrow": G.Workload("fs_narrow", T=1, H=2048, E=16, k=3, F=1024, S=1, Fs=128,
+                            seed=0x5EED010E),
+    # FFN 4096 routed experts (cross-workgroup down combine) beside a 2048 shared one
+    "fs_wide_f": G.Workload("fs_wide_f", T=1, H=2048, E=12, k=2, F=4096, S=1, Fs=2048,
+                            seed=0x5EED010F),
 }
 
 
@@ -303,7 +310,7 @@ def test_cross_workgroup_combine_deterministic_and_poison_proof(name):
     assert max_err_ratio(outs[0], ref["out"])[0] <= TOL
 
 
-@pytest.mark.parametrize("name", ["tiny", "k3_batch1", "wide_f"])
+@pytest.mark.parametrize("name", ["tiny", "k3_batch1", "wide_f", "fs_wide_f"])
 def test_graph_replay_matches_eager(name):
     """One layer captured in a HIP graph, replayed with new inputs copied in
     between; every replay equals the eager call on the same input, and the
