@@ -164,7 +164,7 @@ def counters(fetch_csv: str, write_csv: str) -> str:
             continue
         b = int(round(fetch[k] * 1024 * f_fetch + write[k] * 1024 * f_write))
         out.append(f"{k:28s} {n_f[k]:8d} {fetch[k]:12.1f} {write[k]:10.1f} {b:17d}")
-        if k == "k2_gateup (stand-alone)":
+        if k in ("k2_gateup (in layer)", "kb_gateup"):  # the kernel bench.py's roofline names
             traffic = b
     out.append(f"kernel_source_sha256_16: {source_digest()}")
     out.append(f"batched_source_sha256_16: {source_digest(BATCHED_SRC)}")
