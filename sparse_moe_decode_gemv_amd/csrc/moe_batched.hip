@@ -46,6 +46,8 @@
 #include "moe_internal.h"
 #include "moe_topk.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -250,10 +252,16 @@ __device__ __forceinline__ int token_of(const LayerTB& L, int pid) {
 // Workgroup items (group, 4 consecutive 16-row tiles) in group-major order, so
 // the workgroups running together read consecutive rows of one expert.  The
 // four waves share the group's tokens: per K chunk of KC elements the
-// workgroup stages 16 tokens' activations in LDS (rows padded by 16 bytes so
-// that the 16 lanes of a ds_read_b128 phase hit distinct banks), double
-// buffered; each wave streams its own 16 gate and 16 up rows in registers
-// (two statically named register sets).
+// workgroup stages up to 32 tokens' activations in LDS (two 16-token MFMA
+// tiles; rows padded by 16 bytes so that the 16 lanes of a ds_read_b128 phase
+// hit distinct banks), double buffered; each wave streams its own 16 gate and
+// 16 up rows in registers (two statically named register sets) and multiplies
+// each decoded weight fragment into both tiles.  A group of m tokens thus
+// streams its weights ceil(m / 32) times (with skewed routing the hot experts
+// hold 17..32 tokens; only the shared expert's group, which holds every
+// token, exceeds 32 at batch 64).  When a pass holds 16 tokens or fewer the
+// second tile is neither staged (empty descriptor) nor multiplied (a
+// workgroup-uniform branch around products only).
 //
 // Pipeline of chunk c (one barrier per chunk): products of chunk c, then
 // the requests for chunk c + 2 (token activations into staging registers,
@@ -266,6 +274,10 @@ __device__ __forceinline__ int token_of(const LayerTB& L, int pid) {
 template <int KC>
 struct TokLds {
   uint4 b[2][16][KC / 8 + 1];
+};
+template <int KC>
+struct TokLds2 {  // two 16-token tiles per buffer
+  uint4 b[2][32][KC / 8 + 1];
 };
 
 template <int KC>
@@ -359,17 +371,26 @@ __device__ __forceinline__ void gu_load_a(GuRegs<KC>& R, const Tile& G, const Ti
   ld_tile<KC>(R.au, R.su, U, voc, vos, c, nch);
 }
 
+// Products of one chunk: token tile 0 (LDS rows 0..15) always, tile 1 (rows
+// 16..31) when `two` (workgroup-uniform), from the same decoded fragments.
 template <int KC>
 __device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, const uint4 (*bt)[KC / 8 + 1], int q,
-                                       int r, f32x4& cg, f32x4& cu) {
+                                       int r, bool two, f32x4 (&cg)[2], f32x4 (&cu)[2]) {
 #pragma unroll
   for (int kk = 0; kk < KC / 128; ++kk) {
     const float fg = scale_of(R.sg, kk, q, r), fu = scale_of(R.su, kk, q, r);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const bf16x8 bv = as_bf16x8(bt[r][kk * 16 + 4 * q + s]);
-      cg = mfma16(fp4x8_to_bf16(dword_of(R.ag[kk], s), fg), bv, cg);
-      cu = mfma16(fp4x8_to_bf16(dword_of(R.au[kk], s), fu), bv, cu);
+      const bf16x8 ag = fp4x8_to_bf16(dword_of(R.ag[kk], s), fg);
+      const bf16x8 au = fp4x8_to_bf16(dword_of(R.au[kk], s), fu);
+      const bf16x8 b0 = as_bf16x8(bt[r][kk * 16 + 4 * q + s]);
+      cg[0] = mfma16(ag, b0, cg[0]);
+      cu[0] = mfma16(au, b0, cu[0]);
+      if (two) {
+        const bf16x8 b1 = as_bf16x8(bt[16 + r][kk * 16 + 4 * q + s]);
+        cg[1] = mfma16(ag, b1, cg[1]);
+        cu[1] = mfma16(au, b1, cu[1]);
+      }
     }
   }
 }
@@ -378,17 +399,105 @@ __device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, const uint4 (*bt)[KC
 // is then unrolled whole, so that the wait counts carry no loop back-edge
 // merge (with one, the compiler's waits become conservative and every chunk
 // waits for the requests just issued).
-template <int KC, int NCH>
-__global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
-  __shared__ TokLds<KC> S;
-  constexpr int PER = KC / 128;  // staged uint4 per thread per chunk
+// One pass of an item over the weights: tokens n0 .. n0 + 15 (TWO: n0 + 31)
+// of the group.  The one-tile and two-tile passes are separate code paths,
+// chosen per pass, so neither carries the other's requests.
+template <int KC, int NCH, bool TWO, class Lds>
+__device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G, const Tile& U,
+                                        uint32_t voc, uint32_t vos, int start, int m, int n0, int rq) {
+  constexpr int PER = KC / 128;  // staged uint4 per thread per chunk and tile
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
+  const int nch = NCH ? NCH : L.H / KC;
+  const int sc = tid >> 4, sj = tid & 15;  // staging: token rows sc (and 16 + sc), first piece (stride 16)
+  const auto rx = buf_rsrc(L.x, (uint32_t)L.T * (uint32_t)L.H * 2u), rx0 = buf_rsrc(L.x, 0u);
+  const int cs0 = n0 + sc < m ? n0 + sc : m - 1, cs1 = n0 + 16 + sc < m ? n0 + 16 + sc : m - 1;
+  const uint32_t xv0 = (uint32_t)token_of(L, L.order[start + cs0]) * (uint32_t)L.H * 2u + 16u * (uint32_t)sj;
+  const uint32_t xv1 = TWO ? (uint32_t)token_of(L, L.order[start + cs1]) * (uint32_t)L.H * 2u + 16u * (uint32_t)sj : 0u;
+  auto xso = [&](int c) { return (uint32_t)(c < nch ? c : nch - 1) * (uint32_t)(KC * 2); };
+  // this wave stages rows 4 wid .. 4 wid + 3 of each tile; past the group's
+  // tokens it requests nothing (empty descriptor: zeros, whose products are
+  // dropped)
+  const auto rw0 = 4 * wid < m - n0 ? rx : rx0, rw1 = 16 + 4 * wid < m - n0 ? rx : rx0;
+  f32x4 cg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4 cu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  GuRegs<KC> A0, A1;
+  Stage<PER> xa0, xa1, xb0, xb1;
+  xa0.load(rw0, xv0, xso(0));
+  if (TWO) xa1.load(rw1, xv1, xso(0));
+  __builtin_amdgcn_sched_barrier(0);
+  gu_load_a<KC>(A0, G, U, voc, vos, 0, nch);
+  __builtin_amdgcn_sched_barrier(0);
+  xb0.load(rw0, xv0, xso(1));
+  if (TWO) xb1.load(rw1, xv1, xso(1));
+  __builtin_amdgcn_sched_barrier(0);
+  gu_load_a<KC>(A1, G, U, voc, vos, 1, nch);
+  __builtin_amdgcn_sched_barrier(0);
+  xa0.store(&S.b[0][sc][sj]);
+  if (TWO) xa1.store(&S.b[0][16 + sc][sj]);
+  __syncthreads();
+  // chunk c: weights in Ac, activations in LDS buffer bu; chunk c + 1's
+  // weights and activations (xs) in flight; xl takes chunk c + 2's
+  auto step = [&](int c, GuRegs<KC>& Ac, Stage<PER>& xl0, Stage<PER>& xl1, const Stage<PER>& xs0,
+                  const Stage<PER>& xs1, const uint4 (*bu)[KC / 8 + 1], uint4 (*bs)[KC / 8 + 1]) {
+    gu_mma<KC>(Ac, bu, q, r, TWO, cg, cu);
+    if (!NCH || c + 2 < nch) {
+      xl0.load(rw0, xv0, xso(c + 2));
+      if (TWO) xl1.load(rw1, xv1, xso(c + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      gu_load_a<KC>(Ac, G, U, voc, vos, c + 2, nch);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!NCH || c + 1 < nch) {
+      xs0.store(&bs[sc][sj]);
+      if (TWO) xs1.store(&bs[16 + sc][sj]);
+    }
+    __syncthreads();
+  };
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int c = 0; c < NCH; c += 2) {
+      step(c, A0, xa0, xa1, xb0, xb1, S.b[0], S.b[1]);
+      if (c + 1 < NCH) step(c + 1, A1, xb0, xb1, xa0, xa1, S.b[1], S.b[0]);
+    }
+  } else {
+    for (int c = 0; c < nch; c += 2) {
+      step(c, A0, xa0, xa1, xb0, xb1, S.b[0], S.b[1]);
+      if (c + 1 >= nch) break;
+      step(c + 1, A1, xb0, xb1, xa0, xa1, S.b[1], S.b[0]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < (TWO ? 2 : 1); ++t) {
+    if (n0 + 16 * t + r < m) {
+      const size_t o = (size_t)(start + n0 + 16 * t + r) * L.F + (rq * kWv + wid) * kTileRows + 4 * q;
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = silu(cg[t][i]) * cu[t][i];
+        hi[i] = f32_to_bf16(a);
+        lo[i] = f32_to_bf16(a - bf16_to_f32(hi[i]));
+      }
+      uint2 vh, vl;
+      vh.x = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
+      vh.y = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+      vl.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+      vl.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+      *reinterpret_cast<uint2*>(L.act_hi + o) = vh;
+      *reinterpret_cast<uint2*>(L.act_lo + o) = vl;
+    }
+  }
+}
+
+// MAXT: token tiles per pass (1 when no group can exceed 16 tokens: T <= 16,
+// which keeps the smaller LDS and one more workgroup per CU).
+template <int KC, int NCH, int MAXT>
+__global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
+  using Lds = typename std::conditional<MAXT == 2, TokLds2<KC>, TokLds<KC>>::type;
+  __shared__ Lds S;
+  const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
   const int ng = ld_uniform(L.ginfo);  // grouping tables: scalar loads
   const int quads = L.F / (kTileRows * kWv);
   const int nitems = ng * quads;
-  const int nch = NCH ? NCH : L.H / KC;
-  const int sc = tid >> 4, sj = tid & 15;  // staging: token row, first piece (stride 16)
-  const auto rx = buf_rsrc(L.x, (uint32_t)L.T * (uint32_t)L.H * 2u), rx0 = buf_rsrc(L.x, 0u);
   for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
     const int g = it / quads, rq = it - g * quads;
     const int e = ld_uniform(L.g_expert + g), start = ld_uniform(L.g_start + g), m = ld_uniform(L.g_count + g);
@@ -398,70 +507,11 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
     const Tile U = make_tile(sh ? L.su_codes : L.u_codes, sh ? L.su_scales : L.u_scales, row0, L.H);
     uint32_t voc, vos;
     tile_offsets<KC>(G, q, r, voc, vos);
-    for (int n0 = 0; n0 < m; n0 += 16) {
-      const int cs = n0 + sc < m ? n0 + sc : m - 1;
-      const uint32_t xvo = (uint32_t)token_of(L, L.order[start + cs]) * (uint32_t)L.H * 2u + 16u * (uint32_t)sj;
-      auto xso = [&](int c) { return (uint32_t)(c < nch ? c : nch - 1) * (uint32_t)(KC * 2); };
-      // this wave stages rows 4 wid .. 4 wid + 3; past the group's tokens it
-      // requests nothing (empty descriptor: zeros, whose products are dropped)
-      const auto rxw = 4 * wid < m - n0 ? rx : rx0;
-      f32x4 cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
-      GuRegs<KC> A0, A1;
-      Stage<PER> xa, xb;
-      xa.load(rxw, xvo, xso(0));
-      __builtin_amdgcn_sched_barrier(0);
-      gu_load_a<KC>(A0, G, U, voc, vos, 0, nch);
-      __builtin_amdgcn_sched_barrier(0);
-      xb.load(rxw, xvo, xso(1));
-      __builtin_amdgcn_sched_barrier(0);
-      gu_load_a<KC>(A1, G, U, voc, vos, 1, nch);
-      __builtin_amdgcn_sched_barrier(0);
-      xa.store(&S.b[0][sc][sj]);
-      __syncthreads();
-      // chunk c: weights in Ac, activations in LDS buffer bu; chunk c + 1's
-      // weights and activations (xs) in flight; xl takes chunk c + 2's
-      auto step = [&](int c, GuRegs<KC>& Ac, Stage<PER>& xl, const Stage<PER>& xs,
-                      const uint4 (*bu)[KC / 8 + 1], uint4 (*bs)[KC / 8 + 1]) {
-        gu_mma<KC>(Ac, bu, q, r, cg, cu);
-        if (!NCH || c + 2 < nch) {
-          xl.load(rxw, xvo, xso(c + 2));
-          __builtin_amdgcn_sched_barrier(0);
-          gu_load_a<KC>(Ac, G, U, voc, vos, c + 2, nch);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (!NCH || c + 1 < nch) xs.store(&bs[sc][sj]);
-        __syncthreads();
-      };
-      if constexpr (NCH > 0) {
-#pragma unroll
-        for (int c = 0; c < NCH; c += 2) {
-          step(c, A0, xa, xb, S.b[0], S.b[1]);
-          if (c + 1 < NCH) step(c + 1, A1, xb, xa, S.b[1], S.b[0]);
-        }
-      } else {
-        for (int c = 0; c < nch; c += 2) {
-          step(c, A0, xa, xb, S.b[0], S.b[1]);
-          if (c + 1 >= nch) break;
-          step(c + 1, A1, xb, xa, S.b[1], S.b[0]);
-        }
-      }
-      if (n0 + r < m) {
-        const size_t o = (size_t)(start + n0 + r) * L.F + (rq * kWv + wid) * kTileRows + 4 * q;
-        uint16_t hi[4], lo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = silu(cg[i]) * cu[i];
-          hi[i] = f32_to_bf16(a);
-          lo[i] = f32_to_bf16(a - bf16_to_f32(hi[i]));
-        }
-        uint2 vh, vl;
-        vh.x = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
-        vh.y = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
-        vl.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
-        vl.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
-        *reinterpret_cast<uint2*>(L.act_hi + o) = vh;
-        *reinterpret_cast<uint2*>(L.act_lo + o) = vl;
-      }
+    for (int n0 = 0; n0 < m; n0 += 16 * MAXT) {
+      if (MAXT == 2 && m - n0 > 16)  // workgroup-uniform
+        gu_pass<KC, NCH, true>(L, S, G, U, voc, vos, start, m, n0, rq);
+      else
+        gu_pass<KC, NCH, false>(L, S, G, U, voc, vos, start, m, n0, rq);
     }
   }
 }
@@ -802,8 +852,12 @@ __global__ __launch_bounds__(kBlk) void kb_rmsnorm(const uint16_t* __restrict__ 
   }
 }
 
-constexpr int kGroupedBlocksPerCU = 4;  // 256-element chunks (93 registers)
-constexpr int kGroupedBlocksPerCU512 = 3;  // 512-element chunks: 157 registers, 3 waves per SIMD
+// Grouped gate/up workgroups per CU (every one resident at once).  Two token
+// tiles per pass: 512-element chunks fit two (180 registers, 66.5 KB LDS),
+// 256-element chunks three (147 registers, 33 KB).  One tile (T <= 16):
+// three with 512-element chunks (137 registers, 33 KB), four with 256 (109).
+constexpr int kGroupedBlocksPerCU[2] = {4, 3};     // 256-element chunks, by tiles - 1
+constexpr int kGroupedBlocksPerCU512[2] = {3, 2};  // 512-element chunks
 constexpr int kDownBlocksPerCU = 2;
 constexpr int kNumCUs = 256;
 
@@ -826,19 +880,26 @@ hipError_t launch_group_tb(const LayerTB& L, hipStream_t s) {
   return hipPeekAtLastError();
 }
 
-hipError_t launch_gateup_tb(const LayerTB& L, hipStream_t s) {
+template <int MAXT>
+hipError_t launch_gateup_tiles(const LayerTB& L, hipStream_t s) {
   // H % 256 == 0 always; 512-element chunks where they divide H
   // every workgroup resident at once (items are dealt out round-robin)
-  const dim3 g512(kNumCUs * kGroupedBlocksPerCU512);
+  const dim3 g512(kNumCUs * kGroupedBlocksPerCU512[MAXT - 1]);
   if (L.H == 7168)
-    MOE_LAUNCH(L.timer, (kb_gateup<512, 14>), g512, dim3(kBlk), 0, s, L);
+    MOE_LAUNCH(L.timer, (kb_gateup<512, 14, MAXT>), g512, dim3(kBlk), 0, s, L);
   else if (L.H == 8192)
-    MOE_LAUNCH(L.timer, (kb_gateup<512, 16>), g512, dim3(kBlk), 0, s, L);
+    MOE_LAUNCH(L.timer, (kb_gateup<512, 16, MAXT>), g512, dim3(kBlk), 0, s, L);
   else if (L.H % 512 == 0)
-    MOE_LAUNCH(L.timer, (kb_gateup<512, 0>), g512, dim3(kBlk), 0, s, L);
+    MOE_LAUNCH(L.timer, (kb_gateup<512, 0, MAXT>), g512, dim3(kBlk), 0, s, L);
   else
-    MOE_LAUNCH(L.timer, (kb_gateup<256, 0>), dim3(kNumCUs * kGroupedBlocksPerCU), dim3(kBlk), 0, s, L);
+    MOE_LAUNCH(L.timer, (kb_gateup<256, 0, MAXT>), dim3(kNumCUs * kGroupedBlocksPerCU[MAXT - 1]), dim3(kBlk), 0, s,
+               L);
   return hipPeekAtLastError();
+}
+
+hipError_t launch_gateup_tb(const LayerTB& L, hipStream_t s) {
+  // a group holds at most T tokens (each token picks an expert once)
+  return L.T > 16 ? launch_gateup_tiles<2>(L, s) : launch_gateup_tiles<1>(L, s);
 }
 
 hipError_t launch_down_tb(const LayerTB& L, hipStream_t s) {
