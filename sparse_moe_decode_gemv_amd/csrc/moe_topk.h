@@ -14,8 +14,7 @@ constexpr int kTopkBlock = 256;
 constexpr int kTopkPerThread = kMaxExperts / kTopkBlock;  // keys per thread
 
 struct TopkLds {
-  alignas(16) uint32_t lmax[kWave];  // wave top-k: lane maxima
-  uint64_t cand[2 * kWave];          // candidates; the upper half takes discarded stores
+  alignas(16) uint64_t cand[2 * kWave];  // candidates; the upper half takes discarded stores
 };
 
 // Sum over the 64 lanes by DPP within rows, then the four row sums (the same
@@ -35,19 +34,21 @@ __device__ __forceinline__ float wave_sum_rows(float v) {
 // Top-k + softmax by ONE wave, without barriers (E <= 1024, k <= 32).  Lane l
 // holds experts 16 l .. 16 l + 15 as order-preserving keys (key[m], 0 for an
 // absent expert); the selection orders experts by larger logit first, then
-// lower index among equal logits.  Every step is a few independent
-// compares per lane (LDS broadcast reads), not a chain of cross-lane reads.
-//  1. T = the k-th largest of the 64 lane maxima: a lane's maximum is T when
-//     at least k lane maxima are >= it and it is the largest such.  At least
-//     k keys are >= T, so every selected key is.
+// lower index among equal logits.
+//  1. T = the k-th largest of the 64 lane maxima (0 when fewer than k lanes
+//     hold experts), found bit by bit from the top: a bit stays set when at
+//     least k lane maxima are >= the prefix with it (one ballot and one
+//     population count per bit, no LDS).  At least k keys are >= T, so every
+//     selected key is.
 //  2. The present keys >= T (C of them, C >= k; about k + 3 for random
 //     logits) are compacted into S.cand as 64-bit composites key << 32 |
 //     ~index, which order the experts exactly as the selection does (a
 //     larger composite ranks first; composites are distinct).  Entries C ..
 //     63 are zero, below every candidate.
-//  3. Candidate j (lane j) counts the composites above its own: its rank.
-//     Ranks below k are the selection, written in that order with their
-//     softmax weights.
+//  3. Candidate j (lane j) counts the composites above its own: its rank
+//     (the candidates are read from LDS in batches of 32 before any compare,
+//     so the reads overlap).  Ranks below k are the selection, written in
+//     that order with their softmax weights.
 // Returns false, writing nothing, when C > 64 (only with many equal logits
 // at the threshold, or E > 64 with fewer than k lanes holding experts); the
 // caller then runs topk_softmax_wave_rounds.
@@ -59,12 +60,12 @@ __device__ inline bool topk_softmax_wave(const uint32_t (&key)[16], int E, int k
   uint32_t lm = 0u;
 #pragma unroll
   for (int m = 0; m < 16; ++m) lm = umax32(lm, key[m]);
-  S.lmax[lane] = lm;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  uint32_t ge[4] = {0u, 0u, 0u, 0u};
+  uint32_t T = 0u;
 #pragma unroll
-  for (int j = 0; j < kWave; ++j) ge[j & 3] += S.lmax[j] >= lm ? 1u : 0u;
-  const uint32_t T = wave_max_u32((ge[0] + ge[1]) + (ge[2] + ge[3]) >= (uint32_t)k ? lm : 0u);
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    T = __builtin_popcountll(__ballot(lm >= c)) >= k ? c : T;
+  }
   // 2. compaction (every lane stores 16 times; non-candidates into the upper half)
   bool take[16];
   uint32_t cnt = 0u;
@@ -88,12 +89,13 @@ __device__ inline bool topk_softmax_wave(const uint32_t (&key)[16], int E, int k
   // 3. ranks
   const uint64_t mine = S.cand[lane];
   uint32_t rk[4] = {0u, 0u, 0u, 0u};
-  if (C <= kWave / 2) {
+  for (int h = 0; h < (C <= kWave / 2 ? kWave / 2 : kWave); h += kWave / 2) {
+    uint64_t v[kWave / 2];
 #pragma unroll
-    for (int j = 0; j < kWave / 2; ++j) rk[j & 3] += S.cand[j] > mine ? 1u : 0u;
-  } else {
+    for (int j = 0; j < kWave / 2; ++j) v[j] = S.cand[h + j];
+    __builtin_amdgcn_sched_barrier(0);  // every read issued before the compares
 #pragma unroll
-    for (int j = 0; j < kWave; ++j) rk[j & 3] += S.cand[j] > mine ? 1u : 0u;
+    for (int j = 0; j < kWave / 2; ++j) rk[j & 3] += v[j] > mine ? 1u : 0u;
   }
   const int r = (int)((rk[0] + rk[1]) + (rk[2] + rk[3]));
   const bool sel = lane < C && r < k;
