@@ -359,7 +359,7 @@ def main():
             log(f"[bench] per-replay µs/layer p10 {spread['p10']} p50 {spread['p50']} "
                 f"p90 {spread['p90']} ({src})")
 
-    kernels = roofline = standalone = ceiling = None
+    kernels = roofline = standalone = ceiling = warm = None
     if not args.no_extras:
         # ---- kernel pass: every kernel of a layer timed by HIP itself
         names = T1_KERNELS if T == 1 else TB_KERNELS
@@ -479,6 +479,31 @@ def main():
         log(f"[bench] streaming read of {STREAM_BYTES >> 30} GiB: {gbps:.0f} GB/s "
             f"({gbps / PEAK_HBM_GBPS:.3f} of peak); layer at {layer_gbps / gbps:.3f} of it")
 
+        # ---- warm number: one token and one weight set, the same call 16
+        # times per graph (caches may keep weights between calls; context
+        # only, the metric above rotates tokens and weight sets)
+        if not args.eager:
+            g_w = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_w):
+                for _ in range(ROT_TOKENS):
+                    step(0)
+            for _ in range(3):
+                g_w.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 8
+            e0.record(stream)
+            for _ in range(reps):
+                g_w.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us_w = e0.elapsed_time(e1) * 1e3 / (reps * ROT_TOKENS * nlayers)
+            warm = {"us_per_layer": round(us_w, 3),
+                    "what": f"one token and one weight set, the same call {ROT_TOKENS} times per "
+                            "graph (weights may stay cached between calls); context, not the metric"}
+            del g_w
+            log(f"[bench] warm, same token and weights: {us_w:.2f} µs/layer")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host ...")
@@ -499,6 +524,7 @@ def main():
                    "timing": "eager" if args.eager else
                    f"hipGraph replays of {rep_steps} steps"},
         "layer_tokens_per_s": round(T * 1e6 / us_layer, 1),
+        "us_per_token": round(ms_per_step * 1e3 / T, 3) if stack else None,
         "layer_hbm": {"bytes": lb, "achieved": round(layer_gbps, 1), "unit": "GB/s",
                       "frac": round(layer_gbps / PEAK_HBM_GBPS, 4)},
         "spread": spread,
@@ -506,6 +532,7 @@ def main():
         "roofline": roofline,
         "gateup_standalone": standalone,
         "stream_read_ceiling": ceiling,
+        "warm_same_inputs": warm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line, ensure_ascii=False), flush=True)
