@@ -509,12 +509,13 @@ __device__ __forceinline__ void k2_body(const LayerT1& L, const uint16_t* __rest
   // the selection's inputs go first and the shared weights last; waiting
   // for the logits then leaves the shared weights in flight.  Wave 0 makes
   // the selection alone (no barrier inside it).
-  // (both requested unconditionally, one of them through an empty
-  // descriptor, so that every path has the same loads in flight)
+  // (both requested unconditionally, the unneeded ones through an empty
+  // descriptor, so that every path has the same loads in flight; only wave 0
+  // reads the logits)
   f32x4 lv[4];
   const int32_t e_in = (int32_t)buf_ld4(buf_rsrc(idx, idx ? 4u * (uint32_t)L.k : 0u),
                                         4u * (threadIdx.x < L.k ? threadIdx.x : 0u), 0u);
-  load_logits16(L.logits, idx ? 0 : L.E, lv);
+  load_logits16(L.logits, (idx || wid != 0) ? 0 : L.E, lv);
   XStage xs;
   stage_x_load(x, L.H, xs);
   uint4 ca[BPLH];
