@@ -54,8 +54,7 @@
  *    F % 128 == 0, 128 <= F <= 8192
  *    1 <= k <= min(E, 32), 1 <= E <= 1024
  *    n_shared in {0, 1}; with a shared expert, shared_ffn % 128 == 0 and
- *      128 <= shared_ffn <= 8192; shared_ffn != ffn only for calls of one
- *      token (the grouped kernels of 2..64 tokens take one FFN width)
+ *      128 <= shared_ffn <= 8192 (it may differ from ffn at any T)
  */
 #ifndef MOE_DECODE_H
 #define MOE_DECODE_H

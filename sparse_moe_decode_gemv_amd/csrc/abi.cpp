@@ -78,7 +78,7 @@ WsGroup ws_group(Carver& c, int E, int T, int k) {
 
 // Batched (T >= 2) layout.
 struct WsTB {
-  size_t reserved, part, idx, wts, act_hi, act_lo, y, xn, total;
+  size_t reserved, part, idx, wts, act_hi, act_lo, act_sh_hi, act_sh_lo, y, xn, total;
   WsGroup grp;
 };
 
@@ -92,8 +92,13 @@ WsTB ws_tb(const moe_shape& s, int T) {
   L.idx = c.take(sizeof(int32_t) * P);
   L.wts = c.take(sizeof(float) * P);
   L.grp = ws_group(c, s.n_experts, T, s.top_k);
-  L.act_hi = c.take(sizeof(uint16_t) * npos * s.ffn);
-  L.act_lo = c.take(sizeof(uint16_t) * npos * s.ffn);
+  // a shared expert of its own width keeps its activations apart: [T][Fs]
+  const bool apart = shared_apart(s);
+  const size_t nrow = apart ? P : npos;
+  L.act_hi = c.take(sizeof(uint16_t) * nrow * s.ffn);
+  L.act_lo = c.take(sizeof(uint16_t) * nrow * s.ffn);
+  L.act_sh_hi = apart ? c.take(sizeof(uint16_t) * (size_t)T * s.shared_ffn) : 0;
+  L.act_sh_lo = apart ? c.take(sizeof(uint16_t) * (size_t)T * s.shared_ffn) : 0;
   L.y = c.take(sizeof(float) * npos * s.hidden);
   L.xn = c.take(sizeof(uint16_t) * (size_t)T * s.hidden);
   L.total = c.o;
@@ -127,12 +132,6 @@ int check_tokens(int32_t T) {
 }
 
 // The grouped (2..64 token) kernels take one FFN width for every group.
-int check_tokens_for(const moe_shape* s, int32_t T) {
-  int rc;
-  if ((rc = check_tokens(T))) return rc;
-  if (T > 1 && shared_apart(*s)) return MOE_ERR_UNSUPPORTED;
-  return MOE_OK;
-}
 
 int check_ws(const moe_shape* s, int32_t T, const void* ws, size_t ws_bytes) {
   if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
@@ -234,6 +233,11 @@ LayerTB make_layer_tb(const moe_shape* s, const moe_layer_weights* w, void* ws, 
   set_group(L, W.grp, b);
   L.act_hi = (uint16_t*)(b + W.act_hi);
   L.act_lo = (uint16_t*)(b + W.act_lo);
+  L.Fs = s->n_shared ? s->shared_ffn : s->ffn;
+  if (shared_apart(*s)) {
+    L.act_sh_hi = (uint16_t*)(b + W.act_sh_hi);
+    L.act_sh_lo = (uint16_t*)(b + W.act_sh_lo);
+  }
   L.y = (float*)(b + W.y);
   return L;
 }
@@ -244,11 +248,30 @@ uint16_t* xn_tb(const moe_shape* s, void* ws, int T) { return (uint16_t*)((char*
 // gate/up), K3 (down of every slot + combine) on one stream.
 int run_layer_t1(LayerT1& L, hipStream_t st) { return hip_status(moe::launch_layer_t1(L, st)); }
 
-// One batched layer: router, top-k, grouping, gate/up, down, combine.
+// One batched layer: router, top-k, grouping, gate/up, down, combine.  A
+// shared expert of its own width (its group holds every token, last in the
+// grouping) runs its gate/up and down as passes of their own, at width Fs,
+// with its activations in their own planes; its outputs land in the same
+// per-pair rows, so the combine is unchanged.
 int run_layer_tb(LayerTB& L, hipStream_t st) {
   if (moe::launch_router_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
   if (moe::launch_topk_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
   if (moe::launch_group_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
+  if (L.S && L.act_sh_hi) {
+    LayerTB Lr = L;  // routed groups
+    Lr.gmode = 1;
+    LayerTB Ls = L;  // the shared group, at its own width
+    Ls.gmode = 2;
+    Ls.F = L.Fs;
+    Ls.act_hi = L.act_sh_hi;
+    Ls.act_lo = L.act_sh_lo;
+    Ls.pos0 = L.T * L.k;
+    if (moe::launch_gateup_tb(Lr, st) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_gateup_tb(Ls, st) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_down_tb(Lr, st) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_down_tb(Ls, st) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(moe::launch_combine_tb(L, st));
+  }
   if (moe::launch_gateup_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
   if (moe::launch_down_tb(L, st) != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_combine_tb(L, st));
@@ -271,7 +294,7 @@ const char* moe_status_string(int status) {
 
 int moe_workspace_size(const moe_shape* shape, int32_t max_tokens, size_t* bytes) {
   int rc;
-  if ((rc = check_shape(shape)) || (rc = check_tokens_for(shape, max_tokens))) return rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens(max_tokens))) return rc;
   if (!bytes) return MOE_ERR_INVALID_ARG;
   size_t n = ws_t1(*shape).total;
   if (max_tokens >= 2) {
@@ -340,7 +363,7 @@ int decode_layer(const moe_shape* shape, const moe_layer_weights* w, const uint1
                  int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
                  void* stream, moe::KernelTimer* timer) {
   int rc;
-  if ((rc = check_shape(shape)) || (rc = check_tokens_for(shape, n_tokens))) return rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
   if (n_tokens == 0) return MOE_OK;
   if ((rc = check_weights(shape, w, true))) return rc;
   if (!x || !aligned16(x) || !out || !aligned16(out)) return MOE_ERR_INVALID_ARG;
@@ -436,7 +459,7 @@ int moe_decode_layer_noalloc(const moe_shape* shape, const moe_layer_weights* w,
                              const uint16_t* residual, uint16_t* out, int32_t n_tokens,
                              int32_t* topk_idx_out, float* topk_w_out, void* stream) {
   int rc;
-  if ((rc = check_shape(shape)) || (rc = check_tokens_for(shape, n_tokens))) return rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
   if (n_tokens == 0) return MOE_OK;
   if (ws_needed(*shape, n_tokens) > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
   void* ws = nullptr;
@@ -455,7 +478,7 @@ int moe_decode_stack(const moe_shape* shape, const moe_layer_weights* layers,
                      int32_t n_tokens, int32_t* topk_idx_out, uint16_t* hidden_trace, void* ws,
                      size_t ws_bytes, void* stream) {
   int rc;
-  if ((rc = check_shape(shape)) || (rc = check_tokens_for(shape, n_tokens))) return rc;
+  if ((rc = check_shape(shape)) || (rc = check_tokens(n_tokens))) return rc;
   if (n_layers < 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
   if (n_tokens == 0 || n_layers == 0) return MOE_OK;
   if (!layers || !gammas || !hidden || !aligned16(hidden)) return MOE_ERR_INVALID_ARG;

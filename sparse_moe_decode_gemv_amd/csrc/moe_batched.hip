@@ -241,6 +241,21 @@ __global__ __launch_bounds__(kGroupBlock) void kb_group(LayerTB L) {
     for (int t = tid; t < L.T; t += kGroupBlock) L.order[P + t] = P + t;
 }
 
+// Groups [g0, g1) that a grouped gate/up or down launch covers (gmode).
+__device__ __forceinline__ void group_range(const LayerTB& L, int& g0, int& g1) {
+  const int ng = ld_uniform(L.ginfo);  // grouping tables: scalar loads
+  g0 = L.gmode == 2 ? ng - 1 : 0;
+  g1 = L.gmode == 1 ? ng - L.S : ng;
+}
+
+// Rows of the activation planes a launch reads: every pair, the routed
+// pairs alone (their own planes when the shared expert has its own width),
+// or the shared pairs alone (rows pos0 ..).
+__device__ __forceinline__ uint32_t act_rows(const LayerTB& L) {
+  const int P = L.T * L.k;
+  return (uint32_t)((L.gmode == 1 ? P : P + L.S * L.T) - L.pos0);
+}
+
 // Token of a sorted pair id: routed pairs are t k + j, shared pairs P + t.
 __device__ __forceinline__ int token_of(const LayerTB& L, int pid) {
   const int P = L.T * L.k;
@@ -469,7 +484,7 @@ __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G,
 #pragma unroll
   for (int t = 0; t < (TWO ? 2 : 1); ++t) {
     if (n0 + 16 * t + r < m) {
-      const size_t o = (size_t)(start + n0 + 16 * t + r) * L.F + (rq * kWv + wid) * kTileRows + 4 * q;
+      const size_t o = (size_t)(start + n0 + 16 * t + r - L.pos0) * L.F + (rq * kWv + wid) * kTileRows + 4 * q;
       uint16_t hi[4], lo[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -495,11 +510,12 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
   using Lds = typename std::conditional<MAXT == 2, TokLds2<KC>, TokLds<KC>>::type;
   __shared__ Lds S;
   const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
-  const int ng = ld_uniform(L.ginfo);  // grouping tables: scalar loads
+  int g0, g1;
+  group_range(L, g0, g1);
   const int quads = L.F / (kTileRows * kWv);
-  const int nitems = ng * quads;
+  const int nitems = (g1 - g0) * quads;
   for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
-    const int g = it / quads, rq = it - g * quads;
+    const int gi = it / quads, rq = it - gi * quads, g = g0 + gi;
     const int e = ld_uniform(L.g_expert + g), start = ld_uniform(L.g_start + g), m = ld_uniform(L.g_count + g);
     const bool sh = e >= L.E;
     const size_t row0 = (sh ? 0 : (size_t)e * L.F) + (size_t)(rq * kWv + wid) * kTileRows;
@@ -558,17 +574,18 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
   __shared__ TokLds<KC> Sh, Sl;
   constexpr int PER = KC / 128;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
-  const int ng = ld_uniform(L.ginfo);  // grouping tables: scalar loads
+  int g0, g1;
+  group_range(L, g0, g1);
   const int slabs = L.H / (kTileRows * kDnWaves);
-  const int nitems = ng * slabs;
+  const int nitems = (g1 - g0) * slabs;
   const int nch = L.F / KC;
   const bool st_lo = wid >= kDnWaves / 2;  // staging: waves 0..3 stage a_hi, 4..7 a_lo
   const int sc = (tid & 255) >> 4, sj = tid & 15;  // token row, first piece (stride 16)
-  // staged pairs: a_hi (waves 0..3) or a_lo (waves 4..7), [pairs][F] bf16
-  const uint32_t npairs = (uint32_t)(L.T * L.k + L.S * L.T);
-  const auto ra = buf_rsrc(st_lo ? L.act_lo : L.act_hi, npairs * (uint32_t)L.F * 2u);
+  // staged pairs: a_hi (waves 0..3) or a_lo (waves 4..7), [rows][F] bf16
+  const uint32_t nrows = act_rows(L);
+  const auto ra = buf_rsrc(st_lo ? L.act_lo : L.act_hi, nrows * (uint32_t)L.F * 2u);
   for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
-    const int g = it / slabs, sb = it - g * slabs;
+    const int gi = it / slabs, sb = it - gi * slabs, g = g0 + gi;
     const int e = ld_uniform(L.g_expert + g), start = ld_uniform(L.g_start + g), m = ld_uniform(L.g_count + g);
     const bool sh = e >= L.E;
     const int rt = sb * kDnWaves + wid;
@@ -578,7 +595,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
     tile_offsets<KC>(D, q, r, voc, vos);
     for (int n0 = 0; n0 < m; n0 += 16) {
       const int cs = n0 + sc < m ? n0 + sc : m - 1;
-      const uint32_t xvo = (uint32_t)(start + cs) * (uint32_t)L.F * 2u + 16u * (uint32_t)sj;
+      const uint32_t xvo = (uint32_t)(start + cs - L.pos0) * (uint32_t)L.F * 2u + 16u * (uint32_t)sj;
       auto xso = [&](int c) { return (uint32_t)(c < nch ? c : nch - 1) * (uint32_t)(KC * 2); };
       uint4 (*sbuf0)[KC / 8 + 1] = st_lo ? Sl.b[0] : Sh.b[0];
       uint4 (*sbuf1)[KC / 8 + 1] = st_lo ? Sl.b[1] : Sh.b[1];
@@ -636,16 +653,18 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
   __shared__ TokLds<KC> Sh, Sl;
   constexpr int PER = KC / 128;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
-  const int ng = ld_uniform(L.ginfo);  // grouping tables: scalar loads
+  int g0, g1;
+  group_range(L, g0, g1);
   const int slabs = L.H / (kTileRows * kDnWaves);
-  const int nitems = ng * slabs;
+  const int nitems = (g1 - g0) * slabs;
   // staging: waves 0..3 stage a_hi, 4..7 a_lo (a wave-uniform choice, so the
   // descriptor stays in scalar registers)
   const bool st_lo = wid >= kDnWaves / 2;
   const int sc = (tid & 255) >> 4, sj = tid & 15;  // token row, first piece (stride 16)
   const uint32_t npairs = (uint32_t)(L.T * L.k + L.S * L.T);
+  const uint32_t nrows = act_rows(L);
   const uint16_t* abase = st_lo ? L.act_lo : L.act_hi;
-  const auto ra = buf_rsrc(abase, npairs * (uint32_t)L.F * 2u), ra0 = buf_rsrc(abase, 0u);
+  const auto ra = buf_rsrc(abase, nrows * (uint32_t)L.F * 2u), ra0 = buf_rsrc(abase, 0u);
   const auto ry = buf_rsrc(L.y, npairs * (uint32_t)L.H * 4u);
   uint4 (*sbuf[2])[KC / 8 + 1] = {st_lo ? Sl.b[0] : Sh.b[0], st_lo ? Sl.b[1] : Sh.b[1]};
 
@@ -659,7 +678,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
     Unit u;
     u.live = it < nitems;
     const int itc = u.live ? it : nitems - 1;
-    const int g = itc / slabs, sb = itc - g * slabs;
+    const int gi = itc / slabs, sb = itc - gi * slabs, g = g0 + gi;
     const int e = ld_uniform(L.g_expert + g), start = ld_uniform(L.g_start + g), m = ld_uniform(L.g_count + g);
     const bool sh = e >= L.E;
     u.rt = sb * kDnWaves + wid;
@@ -667,7 +686,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
     u.D = make_tile(sh ? L.sd_codes : L.d_codes, sh ? L.sd_scales : L.d_scales, row0, L.F);
     tile_offsets<KC>(u.D, q, r, u.voc, u.vos);
     const int cs = n0 + sc < m ? n0 + sc : m - 1;
-    u.xvo = (uint32_t)(start + cs) * (uint32_t)L.F * 2u + 16u * (uint32_t)sj;
+    u.xvo = (uint32_t)(start + cs - L.pos0) * (uint32_t)L.F * 2u + 16u * (uint32_t)sj;
     u.pair0 = start + n0;
     u.m = m;
     u.n0 = n0;

@@ -141,6 +141,15 @@ struct LayerTB {
   uint16_t* act_hi;           // [T k + T][F] bf16 leading part of silu(g) u
   uint16_t* act_lo;           // [T k + T][F] bf16 remainder
   float* y;                   // [T k + T][H] expert outputs per sorted pair
+  // shared expert of another width (Fs != F): its activations get planes of
+  // their own, [T][Fs] (else null), and its gate/up and down run as passes
+  // of their own
+  uint16_t *act_sh_hi, *act_sh_lo;
+  int Fs;
+  // groups one grouped gate/up or down launch covers: 0 every group, 1 the
+  // routed ones (the shared group, last when present, is left out), 2 the
+  // shared group alone; act_hi/act_lo row r holds sorted position pos0 + r
+  int gmode, pos0;
   // optional user outputs
   float* logits_out;          // [T][E]
   int32_t* idx_out;           // [T][k]

@@ -29,6 +29,16 @@ SMALL = {
     "h8192": G.Workload("h8192_b", T=1, H=8192, E=16, k=2, F=256, S=1, Fs=256, seed=0x5EED0204),
     # the most experts and the largest top-k the library accepts together
     "emax": G.Workload("emax_b", T=1, H=512, E=1024, k=32, F=128, S=1, Fs=128, seed=0x5EED0205),
+    # a shared expert of its own width: its gate/up and down run as passes of
+    # their own (each pairing of down kernels: generic/generic, the FFN-2048
+    # stream for the routed experts, the FFN-2048 stream for the shared one)
+    "fs_wide": G.Workload("fs_wide_b", T=1, H=1024, E=24, k=4, F=256, S=1, Fs=512, seed=0x5EED0206),
+    "fs_narrow": G.Workload("fs_narrow_b", T=1, H=2048, E=16, k=3, F=1024, S=1, Fs=128,
+                            seed=0x5EED0207),
+    "fs_routed_2048": G.Workload("fs_routed_2048", T=1, H=1024, E=12, k=2, F=2048, S=1, Fs=256,
+                                 seed=0x5EED0208),
+    "fs_shared_2048": G.Workload("fs_shared_2048", T=1, H=768, E=20, k=3, F=256, S=1, Fs=2048,
+                                 seed=0x5EED0209),
 }
 
 
@@ -199,7 +209,7 @@ def test_batch_matches_single_token_calls():
     release_device_layers()
 
 
-@pytest.mark.parametrize("name", ["ragged_shared", "k3_verify8"])
+@pytest.mark.parametrize("name", ["ragged_shared", "fs_narrow", "k3_verify8"])
 def test_batched_graph_replay_matches_eager(name):
     """A batched layer captured in a HIP graph and replayed with new inputs
     copied in between equals the eager call bit for bit, every replay.  At
