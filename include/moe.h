@@ -138,7 +138,8 @@ int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const 
  *   y_e(x) = D_e (silu(G_e x) * (U_e x)), shared expert weight 1
  * rounded once to bf16 (nearest even).  T = 1 runs the single-token kernels;
  * 2 <= T <= 64 groups the (token, slot) pairs by expert and runs grouped
- * MFMA kernels (each selected expert's weights are read once per call).
+ * MFMA kernels (a selected expert's weights are read once per 32 of its
+ * tokens by gate/up and once per 16 by down).
  * x        bf16 [T][H]
  * residual bf16 [T][H] or NULL (no residual); may equal x
  * out      bf16 [T][H]; may equal residual, must not overlap x otherwise
@@ -178,7 +179,8 @@ int moe_decode_layer_noalloc(const moe_shape* shape, const moe_layer_weights* w,
  *             max_kernels (0 <= max_kernels <= MOE_MAX_LAYER_KERNELS)
  *             launch untimed
  * n_kernels   host int32 out: number of kernels the call launched (3 for
- *             one token, 6 for 2..64 tokens)
+ *             one token, 6 for 2..64 tokens; one and two more when the
+ *             shared expert's width differs from the routed experts')
  * The events are recorded eagerly, so the call is not meant for graph
  * capture; read them after synchronising the stream. */
 int moe_decode_layer_timed(const moe_shape* shape, const moe_layer_weights* w,

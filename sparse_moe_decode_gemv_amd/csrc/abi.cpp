@@ -131,8 +131,6 @@ int check_tokens(int32_t T) {
   return MOE_OK;
 }
 
-// The grouped (2..64 token) kernels take one FFN width for every group.
-
 int check_ws(const moe_shape* s, int32_t T, const void* ws, size_t ws_bytes) {
   if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
   if (ws_needed(*s, T) > ws_bytes) return MOE_ERR_WORKSPACE;
