@@ -4,7 +4,8 @@ indices and weights must be identical bit for bit.  Consecutive calls share
 the library's scratch array: a batched K3-shaped call (8 tokens), then a
 smaller single-token K3 call, then a single-token call whose down rows are
 combined across workgroups through the counters at the head of the scratch,
-then graph replays of a captured call."""
+then a batched call whose shared expert has its own width (its own gate/up
+and down launches), then graph replays of a captured call."""
 import numpy as np
 import pytest
 
@@ -14,6 +15,7 @@ from gpu_helpers import (G, M, dev_u16, device_layer, host_u16, pick_tokens,
 pytestmark = pytest.mark.gpu
 
 WIDE = G.Workload("wide_f", T=1, H=2048, E=24, k=4, F=4096, S=1, Fs=4096, seed=0x5EED0105)
+FS_NARROW = G.Workload("fs_narrow_b", T=1, H=2048, E=16, k=3, F=1024, S=1, Fs=128, seed=0x5EED0207)
 
 
 def _tokens(w, dl, T, start):
@@ -52,6 +54,8 @@ def test_noalloc_matches_workspace_entry_on_consecutive_calls():
     dlw = device_layer(WIDE, 0)
     _compare(WIDE, dlw, _tokens(WIDE, dlw, 1, start=30))      # cross-workgroup combine
     _compare(WIDE, dlw, _tokens(WIDE, dlw, 1, start=40))      # counters back at zero
+    dlf = device_layer(FS_NARROW, 0)
+    _compare(FS_NARROW, dlf, _tokens(FS_NARROW, dlf, 17, start=50))  # shared expert apart
     release_device_layers()
 
 
