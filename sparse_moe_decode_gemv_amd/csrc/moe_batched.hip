@@ -1,4 +1,6 @@
-// Batched decode layer (2 <= T <= 64 tokens): six kernels on one stream.
+// Batched decode layer (2 <= T <= 64 tokens): six kernels on one stream
+// (eight when the shared expert's FFN width differs from the routed
+// experts': its group then runs its own gate/up and down launches).
 //
 //  router   logits of all T tokens as bf16 MFMA tiles (16 experts x 16
 //           tokens per fragment), the reduction dimension split KS ways;
@@ -13,8 +15,8 @@
 //           appended as one more group holding every token.
 //  gateup   grouped GEMM per (group, 16-row tile): A = 16 gate rows and 16 up
 //           rows, MXFP4 decoded to exact bf16 in registers; B = the group's
-//           token activations (bf16); fp32 accumulation; SiLU gating in the
-//           epilogue.  The gated activation a is stored as two bf16 parts,
+//           token activations (bf16), one or two 16-token tiles per pass over
+//           the weights; fp32 accumulation; SiLU gating in the epilogue.  The gated activation a is stored as two bf16 parts,
 //           a_hi = bf16(a) and a_lo = bf16(a - a_hi), so that the down GEMM
 //           keeps ~16 significant bits of a on bf16 MFMA.
 //  down     grouped GEMM per (group, 16-row tile of the hidden size) over
