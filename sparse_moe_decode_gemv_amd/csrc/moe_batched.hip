@@ -16,7 +16,8 @@
 //  gateup   grouped GEMM per (group, 16-row tile): A = 16 gate rows and 16 up
 //           rows, MXFP4 decoded to exact bf16 in registers; B = the group's
 //           token activations (bf16), one or two 16-token tiles per pass over
-//           the weights; fp32 accumulation; SiLU gating in the epilogue.  The gated activation a is stored as two bf16 parts,
+//           the weights; fp32 accumulation; SiLU gating in the epilogue.
+//           The gated activation a is stored as two bf16 parts,
 //           a_hi = bf16(a) and a_lo = bf16(a - a_hi), so that the down GEMM
 //           keeps ~16 significant bits of a on bf16 MFMA.
 //  down     grouped GEMM per (group, 16-row tile of the hidden size) over

@@ -41,9 +41,29 @@ def short(name: str) -> str:
     return m.group(1) if m else name[:40]
 
 
+# Headers the kernel sources compile with (project headers only): a digest
+# covers them too, so that a change there also retires a summary.
+KERNEL_HEADERS = [os.path.join(HERE, "csrc", h) for h in ("moe_device.h", "moe_internal.h", "moe_topk.h")] + \
+    [os.path.join(os.path.dirname(HERE), "include", "moe.h")]
+
+
+def code_text(text: str) -> str:
+    """The code of a C++ source: comments removed, runs of blank space
+    collapsed (so that edits to prose do not change the digest)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(path: str = KERNEL_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the code of ``path`` and of the
+    project headers it compiles with, in that order."""
+    h = hashlib.sha256()
+    for f in [path] + KERNEL_HEADERS:
+        with open(f, encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 
 
 def _classify(seq):

@@ -59,3 +59,22 @@ def test_counter_calibration_uses_the_largest_copy(tmp_path):
     # mean of the two launches: 2000 KiB fetched x 2 + 20 KiB written
     line = [l for l in out.splitlines() if l.startswith("kb_gateup")][0]
     assert line.split()[-1] == str((2000 * 2 + 20) * 1024)
+
+
+def test_source_digest_follows_code_not_comments(tmp_path, monkeypatch):
+    """The digest that ties a profile summary to the kernels changes with the
+    code of the source or of a header it compiles with, not with comments or
+    blank space."""
+    from sparse_moe_decode_gemv_amd import profiling as P
+    src, hdr = tmp_path / "k.hip", tmp_path / "h.h"
+    hdr.write_text("int f();\n")
+    monkeypatch.setattr(P, "KERNEL_HEADERS", [str(hdr)])
+    src.write_text("__global__ void k(int* p) { p[0] = 1; }  // store one\n")
+    d0 = P.source_digest(str(src))
+    src.write_text("/* a kernel */\n__global__ void k(int* p) {\n  p[0] = 1;\n}\n")
+    assert P.source_digest(str(src)) == d0
+    src.write_text("__global__ void k(int* p) { p[0] = 2; }\n")
+    assert P.source_digest(str(src)) != d0
+    src.write_text("__global__ void k(int* p) { p[0] = 1; }\n")
+    hdr.write_text("int f(int);\n")
+    assert P.source_digest(str(src)) != d0
