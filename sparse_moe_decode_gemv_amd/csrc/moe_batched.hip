@@ -301,7 +301,13 @@ struct TokLds2 {  // two 16-token tiles per buffer
 template <int KC>
 struct GuRegs {
   uint4 ag[KC / 128], au[KC / 128];
-  uint32_t sg, su;  // scale dwords (see ld_tile)
+  uint32_t sg, su;  // scale dwords (see ld_tile), when not preloaded
+};
+// A tile's scale dwords for every chunk (NCH fixed at compile time): entry c
+// is what ld_tile would request for chunk c.  Requested once per work item.
+template <int NCH>
+struct TileScales {
+  uint32_t g[NCH > 0 ? NCH : 1], u[NCH > 0 ? NCH : 1];
 };
 
 // A wave's 16-row MXFP4 weight tile: codes [16][rowc bytes] and scales
@@ -335,18 +341,36 @@ __device__ __forceinline__ Tile make_tile(const uint8_t* codes, const uint8_t* s
 // rather than one byte request per block), and the byte of block
 // 4 kk + q is later taken from lane (kk, r) with ds_bpermute (scale_of).
 template <int KC>
-__device__ __forceinline__ void ld_tile(uint4 (&a)[KC / 128], uint32_t& sd, const Tile& T, uint32_t voc,
-                                        uint32_t vos, int c, int nch) {
+__device__ __forceinline__ void ld_codes(uint4 (&a)[KC / 128], const Tile& T, uint32_t voc, int c, int nch) {
   const bool live = c < nch;
   const uint32_t cc = (uint32_t)(live ? c : nch - 1);
-  const auto rc = buf_rsrc(T.c, live ? 16u * T.rowc : 0u), rs = buf_rsrc(T.s, live ? 16u * T.rows : 0u);
-  const uint32_t soc = cc * (KC / 2), sos = cc * (KC / 32);
+  const auto rc = buf_rsrc(T.c, live ? 16u * T.rowc : 0u);
+  const uint32_t soc = cc * (KC / 2);
 #pragma unroll
   for (int kk = 0; kk < KC / 128; ++kk) {  // block cc * KC / 32 + 4 kk + q of row r
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(voc + 64u * kk), (int)soc, 0);
     a[kk] = make_uint4(v[0], v[1], v[2], v[3]);
   }
-  sd = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)vos, (int)sos, 0);
+}
+template <int KC>
+__device__ __forceinline__ void ld_tile(uint4 (&a)[KC / 128], uint32_t& sd, const Tile& T, uint32_t voc,
+                                        uint32_t vos, int c, int nch) {
+  ld_codes<KC>(a, T, voc, c, nch);
+  const bool live = c < nch;
+  const uint32_t cc = (uint32_t)(live ? c : nch - 1);
+  const auto rs = buf_rsrc(T.s, live ? 16u * T.rows : 0u);
+  sd = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)vos, (int)(cc * (KC / 32)), 0);
+}
+// Every chunk's scale dword of a tile at once (the same requests ld_tile
+// makes chunk by chunk).  A tile's scale bytes (16 rows x H / 32) span a few
+// dozen lines that each serve several chunks; requested a chunk at a time,
+// the weight stream evicted them from L2 between uses, and the gate/up
+// kernel fetched each scale line about 2.6 times (counted at batch 64).
+template <int KC, int NCH>
+__device__ __forceinline__ void ld_scales(uint32_t (&sd)[NCH], const Tile& T, uint32_t vos) {
+  const auto rs = buf_rsrc(T.s, 16u * T.rows);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) sd[c] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)vos, c * (KC / 32), 0);
 }
 // Per-lane scale offsets of a tile: codes of block q, scale dword q (the
 // last dword for lanes past the chunk's dwords).
@@ -382,21 +406,28 @@ struct Stage {
   }
 };
 
-template <int KC>
+// PRE: the scales were requested for the whole tile (ld_scales): codes only.
+template <int KC, bool PRE>
 __device__ __forceinline__ void gu_load_a(GuRegs<KC>& R, const Tile& G, const Tile& U, uint32_t voc,
                                           uint32_t vos, int c, int nch) {
-  ld_tile<KC>(R.ag, R.sg, G, voc, vos, c, nch);
-  ld_tile<KC>(R.au, R.su, U, voc, vos, c, nch);
+  if (PRE) {
+    ld_codes<KC>(R.ag, G, voc, c, nch);
+    ld_codes<KC>(R.au, U, voc, c, nch);
+  } else {
+    ld_tile<KC>(R.ag, R.sg, G, voc, vos, c, nch);
+    ld_tile<KC>(R.au, R.su, U, voc, vos, c, nch);
+  }
 }
 
 // Products of one chunk: token tile 0 (LDS rows 0..15) always, tile 1 (rows
 // 16..31) when `two` (workgroup-uniform), from the same decoded fragments.
 template <int KC>
-__device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, const uint4 (*bt)[KC / 8 + 1], int q,
-                                       int r, bool two, f32x4 (&cg)[2], f32x4 (&cu)[2]) {
+__device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, uint32_t sg, uint32_t su,
+                                       const uint4 (*bt)[KC / 8 + 1], int q, int r, bool two,
+                                       f32x4 (&cg)[2], f32x4 (&cu)[2]) {
 #pragma unroll
   for (int kk = 0; kk < KC / 128; ++kk) {
-    const float fg = scale_of(R.sg, kk, q, r), fu = scale_of(R.su, kk, q, r);
+    const float fg = scale_of(sg, kk, q, r), fu = scale_of(su, kk, q, r);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 ag = fp4x8_to_bf16(dword_of(R.ag[kk], s), fg);
@@ -419,10 +450,13 @@ __device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, const uint4 (*bt)[KC
 // waits for the requests just issued).
 // One pass of an item over the weights: tokens n0 .. n0 + 15 (TWO: n0 + 31)
 // of the group.  The one-tile and two-tile passes are separate code paths,
-// chosen per pass, so neither carries the other's requests.
+// chosen per pass, so neither carries the other's requests.  With NCH > 0
+// the scales come from TS (requested once per item), else chunk by chunk.
 template <int KC, int NCH, bool TWO, class Lds>
 __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G, const Tile& U,
-                                        uint32_t voc, uint32_t vos, int start, int m, int n0, int rq) {
+                                        const TileScales<NCH>& TS, uint32_t voc, uint32_t vos, int start,
+                                        int m, int n0, int rq) {
+  constexpr bool PRE = NCH > 0;
   constexpr int PER = KC / 128;  // staged uint4 per thread per chunk and tile
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
   const int nch = NCH ? NCH : L.H / KC;
@@ -443,12 +477,12 @@ __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G,
   xa0.load(rw0, xv0, xso(0));
   if (TWO) xa1.load(rw1, xv1, xso(0));
   __builtin_amdgcn_sched_barrier(0);
-  gu_load_a<KC>(A0, G, U, voc, vos, 0, nch);
+  gu_load_a<KC, PRE>(A0, G, U, voc, vos, 0, nch);
   __builtin_amdgcn_sched_barrier(0);
   xb0.load(rw0, xv0, xso(1));
   if (TWO) xb1.load(rw1, xv1, xso(1));
   __builtin_amdgcn_sched_barrier(0);
-  gu_load_a<KC>(A1, G, U, voc, vos, 1, nch);
+  gu_load_a<KC, PRE>(A1, G, U, voc, vos, 1, nch);
   __builtin_amdgcn_sched_barrier(0);
   xa0.store(&S.b[0][sc][sj]);
   if (TWO) xa1.store(&S.b[0][16 + sc][sj]);
@@ -457,12 +491,15 @@ __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G,
   // weights and activations (xs) in flight; xl takes chunk c + 2's
   auto step = [&](int c, GuRegs<KC>& Ac, Stage<PER>& xl0, Stage<PER>& xl1, const Stage<PER>& xs0,
                   const Stage<PER>& xs1, const uint4 (*bu)[KC / 8 + 1], uint4 (*bs)[KC / 8 + 1]) {
-    gu_mma<KC>(Ac, bu, q, r, TWO, cg, cu);
+    if constexpr (PRE)
+      gu_mma<KC>(Ac, TS.g[c], TS.u[c], bu, q, r, TWO, cg, cu);
+    else
+      gu_mma<KC>(Ac, Ac.sg, Ac.su, bu, q, r, TWO, cg, cu);
     if (!NCH || c + 2 < nch) {
       xl0.load(rw0, xv0, xso(c + 2));
       if (TWO) xl1.load(rw1, xv1, xso(c + 2));
       __builtin_amdgcn_sched_barrier(0);
-      gu_load_a<KC>(Ac, G, U, voc, vos, c + 2, nch);
+      gu_load_a<KC, PRE>(Ac, G, U, voc, vos, c + 2, nch);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (!NCH || c + 1 < nch) {
@@ -526,11 +563,16 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
     const Tile U = make_tile(sh ? L.su_codes : L.u_codes, sh ? L.su_scales : L.u_scales, row0, L.H);
     uint32_t voc, vos;
     tile_offsets<KC>(G, q, r, voc, vos);
+    TileScales<NCH> TS;
+    if constexpr (NCH > 0) {
+      ld_scales<KC, NCH>(TS.g, G, vos);
+      ld_scales<KC, NCH>(TS.u, U, vos);
+    }
     for (int n0 = 0; n0 < m; n0 += 16 * MAXT) {
       if (MAXT == 2 && m - n0 > 16)  // workgroup-uniform
-        gu_pass<KC, NCH, true>(L, S, G, U, voc, vos, start, m, n0, rq);
+        gu_pass<KC, NCH, true>(L, S, G, U, TS, voc, vos, start, m, n0, rq);
       else
-        gu_pass<KC, NCH, false>(L, S, G, U, voc, vos, start, m, n0, rq);
+        gu_pass<KC, NCH, false>(L, S, G, U, TS, voc, vos, start, m, n0, rq);
     }
   }
 }
@@ -555,12 +597,18 @@ __device__ __forceinline__ void dn_load_a(DnRegs<KC>& R, const Tile& D, uint32_t
   ld_tile<KC>(R.a, R.sc, D, voc, vos, c, nch);
 }
 
-template <int KC>
+// The scale dword of block group kk comes from lane (kk, r)'s sd (chunk by
+// chunk, see ld_tile) or, with a unit's scales in one quad per lane (QUAD:
+// lane (c, r) holds dwords 4c .. 4c + 3 of row r), from lane (c, r)'s
+// element kk.
+template <int KC, bool QUAD = false>
 __device__ __forceinline__ void dn_mma(const DnRegs<KC>& R, const uint4 (*bh)[KC / 8 + 1],
-                                       const uint4 (*bl)[KC / 8 + 1], int q, int r, f32x4& acc) {
+                                       const uint4 (*bl)[KC / 8 + 1], int q, int r, f32x4& acc,
+                                       const u32x4* quad = nullptr, int c = 0) {
 #pragma unroll
   for (int kk = 0; kk < KC / 128; ++kk) {
-    const float f = scale_of(R.sc, kk, q, r);
+    const float f = QUAD ? e8m0_to_f32(byte_of((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (16 * c + r), (int)(*quad)[kk]), q))
+                         : scale_of(R.sc, kk, q, r);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 av = fp4x8_to_bf16(dword_of(R.a[kk], s), f);
@@ -650,9 +698,15 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
 // chunks per unit, that start was most of a unit's time).  Past the last
 // unit the requests go through empty descriptors and the output store
 // through a range check, so that no request sits under a branch.
+//
+// A unit's scales (16 rows x F / 32 bytes) are requested once, with its
+// first chunk: lane (c, r) takes the 16 bytes of row r that chunk c uses.
+// Requested chunk by chunk, the scale lines were evicted between a unit's
+// chunks and fetched again (about 1.4 times their bytes at batch 64).
 template <int KC, int NCH>
 __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
   static_assert(NCH >= 2 && NCH % 2 == 0, "units alternate register sets by chunk parity");
+  static_assert(NCH == 4 && KC == 512, "a unit's scales are one 16-byte piece per lane (q, r)");
   __shared__ TokLds<KC> Sh, Sl;
   constexpr int PER = KC / 128;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
@@ -698,10 +752,13 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
   // a wave stages rows 4 (wid & 3) .. + 3 of the unit's 16; when they are all
   // past the unit's pairs it requests nothing (empty descriptor: zeros)
   const int srow0 = 4 * (wid & 3);
-  auto load_chunk = [&](const Unit& u, int c, DnRegs<KC>& A, Stage<PER>& X) {
+  auto load_chunk = [&](const Unit& u, int c, DnRegs<KC>& A, Stage<PER>& X, u32x4& Q) {
     X.load(u.live && srow0 < u.m - u.n0 ? ra : ra0, u.xvo, (uint32_t)c * (uint32_t)(KC * 2));
     __builtin_amdgcn_sched_barrier(0);
-    dn_load_a<KC>(A, u.D, u.voc, u.vos, u.live ? c : NCH, NCH);
+    ld_codes<KC>(A.a, u.D, u.voc, u.live ? c : NCH, NCH);
+    if (c == 0)  // the unit's scales: bytes 16 q .. 16 q + 15 of row r
+      Q = __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(u.D.s, u.live ? 16u * u.D.rows : 0u),
+                                                (int)(r * u.D.rows + 16u * (uint32_t)q), 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -710,8 +767,9 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
   Unit cur = unit_at(it, 0);
   DnRegs<KC> A0, A1;
   Stage<PER> xa, xb;
-  load_chunk(cur, 0, A0, xa);
-  load_chunk(cur, 1, A1, xb);
+  u32x4 qc, qn;  // this unit's scales, the next unit's
+  load_chunk(cur, 0, A0, xa, qc);
+  load_chunk(cur, 1, A1, xb, qc);
   xa.store(&sbuf[0][sc][sj]);
   __syncthreads();
   for (;;) {
@@ -723,9 +781,9 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
       DnRegs<KC>& Ac = (c & 1) ? A1 : A0;
       Stage<PER>& xl = (c & 1) ? xb : xa;
       const Stage<PER>& xs = (c & 1) ? xa : xb;
-      dn_mma<KC>(Ac, Sh.b[c & 1], Sl.b[c & 1], q, r, acc);
-      if (c + 2 < NCH) load_chunk(cur, c + 2, Ac, xl);
-      else load_chunk(nxt, c + 2 - NCH, Ac, xl);
+      dn_mma<KC, true>(Ac, Sh.b[c & 1], Sl.b[c & 1], q, r, acc, &qc, c);
+      if (c + 2 < NCH) load_chunk(cur, c + 2, Ac, xl, qc);
+      else load_chunk(nxt, c + 2 - NCH, Ac, xl, qn);
       xs.store(&sbuf[(c + 1) & 1][sc][sj]);
       __syncthreads();
     }
@@ -737,6 +795,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
     if (!nxt.live) break;
     if (!more) it += (int)gridDim.x;
     cur = nxt;
+    qc = qn;  // waits for the next unit's first chunk, which its first products need anyway
   }
 }
 
