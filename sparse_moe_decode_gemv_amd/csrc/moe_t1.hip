@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kBlock) void k1_topk(LayerT1 L) {
 // Two waves per SIMD for the gate/up kernel: three (at most 168 registers)
 // measured no faster, and the selection then covers fewer shared tasks.
 constexpr int kK2WavesPerSimd = 2;
-constexpr int kK2OldRounds = 2;  // task rounds given to the older workgroups only
+constexpr int kK2OldRounds = 3;  // task rounds given to the older workgroups only (2: +0.5 us, 4..6: no better)
 
 // K2: gate/up of the shared expert and of the k selected experts.  With
 // idx == null the experts are selected here: every workgroup runs the same
