@@ -35,10 +35,11 @@
 // 1.2万行代码榨干GB300!…", section 03).  Weight bytes still dominate, so the
 // grouped kernels keep consecutive waves on consecutive row tiles of one
 // expert, request each chunk two chunks ahead with 16-byte buffer loads
-// through L2 (a request covers 64 bytes of a row, and the rest of the line
-// and the tile's scale lines are used by the next requests), and keep the
-// count of requests per chunk low (one scale dword per lane, no staging
-// requests for token rows past the group).
+// through L2 (a request covers 64 bytes of a row, the next one the rest of
+// the line), request a tile's scales once per work item (chunk by chunk,
+// the weight stream evicted the scale lines between uses), and keep the
+// count of requests per chunk low (no staging requests for token rows past
+// the group).
 //
 // MFMA v_mfma_f32_16x16x32_bf16 fragments (lane l = 16 q + r): A holds
 // A[r][8q .. 8q+7], B holds B[8q .. 8q+7][r], the result C[4q .. 4q+3][r].
