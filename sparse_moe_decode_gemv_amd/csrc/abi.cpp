@@ -78,9 +78,15 @@ WsGroup ws_group(Carver& c, int E, int T, int k) {
 
 // Batched (T >= 2) layout.
 struct WsTB {
-  size_t reserved, part, idx, wts, act_hi, act_lo, act_sh_hi, act_sh_lo, y, xn, total;
+  size_t reserved, part, idx, wts, act_hi, act_lo, act_sh_hi, act_sh_lo, y, xn, pass_group, pass_n0, total;
   WsGroup grp;
 };
+
+// Passes of at most 16 pairs over all groups: at most one per group plus
+// one per 16 pairs.
+size_t max_passes(const moe_shape& s, int T) {
+  return (size_t)s.n_experts + 1 + ((size_t)T * (s.top_k + s.n_shared) + 15) / 16;
+}
 
 WsTB ws_tb(const moe_shape& s, int T) {
   WsTB L{};
@@ -101,6 +107,8 @@ WsTB ws_tb(const moe_shape& s, int T) {
   L.act_sh_lo = apart ? c.take(sizeof(uint16_t) * (size_t)T * s.shared_ffn) : 0;
   L.y = c.take(sizeof(float) * npos * s.hidden);
   L.xn = c.take(sizeof(uint16_t) * (size_t)T * s.hidden);
+  L.pass_group = c.take(sizeof(int32_t) * max_passes(s, T));
+  L.pass_n0 = c.take(sizeof(int32_t) * max_passes(s, T));
   L.total = c.o;
   return L;
 }
@@ -229,6 +237,8 @@ LayerTB make_layer_tb(const moe_shape* s, const moe_layer_weights* w, void* ws, 
   L.idx = (int32_t*)(b + W.idx);
   L.wts = (float*)(b + W.wts);
   set_group(L, W.grp, b);
+  L.pass_group = (int32_t*)(b + W.pass_group);
+  L.pass_n0 = (int32_t*)(b + W.pass_n0);
   L.act_hi = (uint16_t*)(b + W.act_hi);
   L.act_lo = (uint16_t*)(b + W.act_lo);
   L.Fs = s->n_shared ? s->shared_ffn : s->ffn;

@@ -206,8 +206,10 @@ __global__ __launch_bounds__(kGroupBlock) void kb_group(LayerTB L) {
   __syncthreads();
   const int cnt = tid < L.E ? __popc(s_mask[tid][0]) + __popc(s_mask[tid][1]) : 0;
   const int act = cnt > 0 ? 1 : 0;
+  const int npass = (cnt + 15) / 16;  // passes of at most 16 pairs
   const int off_incl = block_incl_scan(cnt, s_wsum);
   const int act_incl = block_incl_scan(act, s_wsum);
+  const int pass_incl = block_incl_scan(npass, s_wsum);
   const int off = off_incl - cnt;
   s_off[tid] = off;
   if (act) {
@@ -215,6 +217,11 @@ __global__ __launch_bounds__(kGroupBlock) void kb_group(LayerTB L) {
     L.g_expert[a] = tid;
     L.g_start[a] = off;
     L.g_count[a] = cnt;
+    if (L.pass_group)
+      for (int q = 0; q < npass; ++q) {
+        L.pass_group[pass_incl - npass + q] = a;
+        L.pass_n0[pass_incl - npass + q] = 16 * q;
+      }
   }
   if (L.offsets_out && tid < L.E) L.offsets_out[tid] = off;
   if (tid == kGroupBlock - 1) {
@@ -224,6 +231,15 @@ __global__ __launch_bounds__(kGroupBlock) void kb_group(LayerTB L) {
       L.g_expert[nact] = L.E;
       L.g_start[nact] = P;
       L.g_count[nact] = L.T;
+    }
+    if (L.pass_group) {
+      const int nps = L.S ? (L.T + 15) / 16 : 0;  // the shared group's passes
+      for (int q = 0; q < nps; ++q) {
+        L.pass_group[pass_incl + q] = nact;
+        L.pass_n0[pass_incl + q] = 16 * q;
+      }
+      L.ginfo[1] = pass_incl;
+      L.ginfo[2] = pass_incl + nps;
     }
     if (L.offsets_out) L.offsets_out[L.E] = off_incl;
   }
@@ -250,6 +266,13 @@ __device__ __forceinline__ void group_range(const LayerTB& L, int& g0, int& g1) 
   const int ng = ld_uniform(L.ginfo);  // grouping tables: scalar loads
   g0 = L.gmode == 2 ? ng - 1 : 0;
   g1 = L.gmode == 1 ? ng - L.S : ng;
+}
+
+// Passes [v0, v1) that a down launch covers (gmode, as group_range).
+__device__ __forceinline__ void pass_range(const LayerTB& L, int& v0, int& v1) {
+  const int nr = ld_uniform(L.ginfo + 1), na = ld_uniform(L.ginfo + 2);
+  v0 = L.gmode == 2 ? nr : 0;
+  v1 = L.gmode == 1 ? nr : na;
 }
 
 // Rows of the activation planes a launch reads: every pair, the routed
@@ -692,8 +715,17 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
 }
 
 // The down kernel for an even, compile-time chunk count (FFN 2048: four
-// chunks of 512).  A wave's work is the sequence of its (item, token tile)
-// units, and it runs that sequence as one stream of chunks: the last two
+// chunks of 512).  A unit is (pass, slab of 8 row tiles): a pass is at most
+// 16 pairs of one group (the grouping kernel lists the passes in group
+// order), and units are dealt out pass-major, so the passes of a group that
+// holds more than 16 pairs reach the same slab `slabs` units apart -- on
+// the same XCD when slabs is a multiple of 8 (hidden 7168: 56), and at about
+// the same time -- and read its weights through one L2.  (With the passes of
+// a slab run one after another by one workgroup, the weights were fetched
+// again for each pass.)  PASSES = false (at most 16 tokens, so every group
+// is one pass) walks the groups directly.  A wave's work is the sequence of
+// its units, and it
+// runs that sequence as one stream of chunks: the last two
 // chunks of a unit request the next unit's first two, so a unit starts with
 // its weights already in flight instead of a cold pipeline (with four
 // chunks per unit, that start was most of a unit's time).  Past the last
@@ -704,17 +736,18 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
 // first chunk: lane (c, r) takes the 16 bytes of row r that chunk c uses.
 // Requested chunk by chunk, the scale lines were evicted between a unit's
 // chunks and fetched again (about 1.4 times their bytes at batch 64).
-template <int KC, int NCH>
+template <int KC, int NCH, bool PASSES>
 __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
   static_assert(NCH >= 2 && NCH % 2 == 0, "units alternate register sets by chunk parity");
   static_assert(NCH == 4 && KC == 512, "a unit's scales are one 16-byte piece per lane (q, r)");
   __shared__ TokLds<KC> Sh, Sl;
   constexpr int PER = KC / 128;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
-  int g0, g1;
-  group_range(L, g0, g1);
+  int v0, v1;
+  if (PASSES) pass_range(L, v0, v1);
+  else group_range(L, v0, v1);
   const int slabs = L.H / (kTileRows * kDnWaves);
-  const int nitems = (g1 - g0) * slabs;
+  const int nitems = (v1 - v0) * slabs;
   // staging: waves 0..3 stage a_hi, 4..7 a_lo (a wave-uniform choice, so the
   // descriptor stays in scalar registers)
   const bool st_lo = wid >= kDnWaves / 2;
@@ -732,11 +765,12 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
     int pair0, m, n0, rt;
     bool live;
   };
-  auto unit_at = [&](int it, int n0) {
+  auto unit_at = [&](int it) {
     Unit u;
     u.live = it < nitems;
     const int itc = u.live ? it : nitems - 1;
-    const int gi = itc / slabs, sb = itc - gi * slabs, g = g0 + gi;
+    const int vi = itc / slabs, sb = itc - vi * slabs, v = v0 + vi;
+    const int g = PASSES ? ld_uniform(L.pass_group + v) : v, n0 = PASSES ? ld_uniform(L.pass_n0 + v) : 0;
     const int e = ld_uniform(L.g_expert + g), start = ld_uniform(L.g_start + g), m = ld_uniform(L.g_count + g);
     const bool sh = e >= L.E;
     u.rt = sb * kDnWaves + wid;
@@ -765,7 +799,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
 
   int it = blockIdx.x;
   if (it >= nitems) return;
-  Unit cur = unit_at(it, 0);
+  Unit cur = unit_at(it);
   DnRegs<KC> A0, A1;
   Stage<PER> xa, xb;
   u32x4 qc, qn;  // this unit's scales, the next unit's
@@ -774,8 +808,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
   xa.store(&sbuf[0][sc][sj]);
   __syncthreads();
   for (;;) {
-    const bool more = cur.n0 + 16 < cur.m;
-    const Unit nxt = unit_at(more ? it : it + (int)gridDim.x, more ? cur.n0 + 16 : 0);
+    const Unit nxt = unit_at(it + (int)gridDim.x);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -794,7 +827,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
                            : 0xFFFFFFF0u;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ry, (int)yo, 0, 0);
     if (!nxt.live) break;
-    if (!more) it += (int)gridDim.x;
+    it += (int)gridDim.x;
     cur = nxt;
     qc = qn;  // waits for the next unit's first chunk, which its first products need anyway
   }
@@ -986,8 +1019,11 @@ hipError_t launch_gateup_tb(const LayerTB& L, hipStream_t s) {
 
 hipError_t launch_down_tb(const LayerTB& L, hipStream_t s) {
   const dim3 grid(kNumCUs * kDownBlocksPerCU);
-  if (L.F == 2048)
-    MOE_LAUNCH(L.timer, (kb_down_flat<512, 4>), grid, dim3(kDnBlock), 0, s, L);
+  // a group holds at most T pairs: more than one pass only when T > 16
+  if (L.F == 2048 && L.T > 16)
+    MOE_LAUNCH(L.timer, (kb_down_flat<512, 4, true>), grid, dim3(kDnBlock), 0, s, L);
+  else if (L.F == 2048)
+    MOE_LAUNCH(L.timer, (kb_down_flat<512, 4, false>), grid, dim3(kDnBlock), 0, s, L);
   else if (L.F % 512 == 0)
     MOE_LAUNCH(L.timer, kb_down<512>, grid, dim3(kDnBlock), 0, s, L);
   else if (L.F % 256 == 0)

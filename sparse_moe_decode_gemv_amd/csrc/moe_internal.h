@@ -132,12 +132,17 @@ struct LayerTB {
   float* part;                // [KS][T][E] partial router logits
   int32_t* idx;               // [T][k]
   float* wts;                 // [T][k]
-  int32_t* ginfo;             // [0]: number of groups (active experts + shared)
+  int32_t* ginfo;             // [0]: number of groups (active experts + shared);
+                              // [1], [2]: passes of the routed groups, of all groups
   int32_t* g_expert;          // [E + 1] expert of each group (E: the shared expert)
   int32_t* g_start;           // [E + 1] first sorted position of the group
   int32_t* g_count;           // [E + 1] pairs in the group
   int32_t* order;             // [T k + T] pair id at each sorted position
   int32_t* pos_of;            // [T k] sorted position of pair t k + j
+  // the groups cut into passes of at most 16 pairs, in group order (pass p
+  // of group g holds its pairs 16 p .. 16 p + 15); null: not written
+  int32_t* pass_group;        // [passes] group of each pass
+  int32_t* pass_n0;           // [passes] first pair of the pass within its group
   uint16_t* act_hi;           // [T k + T][F] bf16 leading part of silu(g) u
   uint16_t* act_lo;           // [T k + T][F] bf16 remainder
   float* y;                   // [T k + T][H] expert outputs per sorted pair
