@@ -156,7 +156,7 @@ int moe_decode_layer(const moe_shape* shape, const moe_layer_weights* w, const u
  * (16 MiB) per GPU, held until the process ends; nothing is allocated or
  * freed by any call.  Shapes whose workspace (moe_workspace_size for
  * n_tokens) exceeds that size return MOE_ERR_UNSUPPORTED: every
- * single-token shape fits, and the K3-sized layer fits up to about 23
+ * single-token shape fits, and the K3-sized layer fits up to 24
  * tokens.  Every call on a GPU shares that GPU's array: calls that overlap
  * in time on one GPU (different streams, or host threads) race and give
  * undefined results; serialise them.  The first call on each device looks

@@ -167,6 +167,10 @@ def test_noalloc_entry_rejects_shapes_beyond_its_scratch_on_the_host():
                                       None) == M.MOE_ERR_INVALID_ARG
     assert L.moe_decode_layer_noalloc(ctypes.byref(s), ctypes.byref(w), FAKE, FAKE, FAKE, 0, None,
                                       None, None) == M.MOE_OK
+    # the limit the header states: the K3-sized layer fits up to 24 tokens
+    assert M.workspace_size(s, 24) <= M.MOE_NOALLOC_SCRATCH_BYTES < M.workspace_size(s, 25)
+    assert L.moe_decode_layer_noalloc(ctypes.byref(s), ctypes.byref(w), FAKE, FAKE,
+                                      FAKE + (1 << 20), 25, None, None, None) == M.MOE_ERR_UNSUPPORTED
 
 
 def test_shared_expert_of_another_width():
