@@ -138,8 +138,9 @@ int moe_expert_gateup(const moe_shape* shape, const moe_layer_weights* w, const 
  *   y_e(x) = D_e (silu(G_e x) * (U_e x)), shared expert weight 1
  * rounded once to bf16 (nearest even).  T = 1 runs the single-token kernels;
  * 2 <= T <= 64 groups the (token, slot) pairs by expert and runs grouped
- * MFMA kernels (a selected expert's weights are read once per 32 of its
- * tokens by gate/up and once per 16 by down).
+ * MFMA kernels (gate/up streams a selected expert's weights once per 32 of
+ * its tokens; down requests them once per 16, and those passes run side by
+ * side on one XCD, so the repeats are mostly served by its L2).
  * x        bf16 [T][H]
  * residual bf16 [T][H] or NULL (no residual); may equal x
  * out      bf16 [T][H]; may equal residual, must not overlap x otherwise
