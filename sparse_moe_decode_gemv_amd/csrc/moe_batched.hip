@@ -724,8 +724,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down(LayerTB L) {
 // a slab run one after another by one workgroup, the weights were fetched
 // again for each pass.)  PASSES = false (at most 16 tokens, so every group
 // is one pass) walks the groups directly.  A wave's work is the sequence of
-// its units, and it
-// runs that sequence as one stream of chunks: the last two
+// its units, and it runs that sequence as one stream of chunks: the last two
 // chunks of a unit request the next unit's first two, so a unit starts with
 // its weights already in flight instead of a cold pipeline (with four
 // chunks per unit, that start was most of a unit's time).  Past the last
