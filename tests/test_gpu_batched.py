@@ -209,16 +209,18 @@ def test_batch_matches_single_token_calls():
     release_device_layers()
 
 
-@pytest.mark.parametrize("name", ["ragged_shared", "fs_narrow", "k3_verify8"])
-def test_batched_graph_replay_matches_eager(name):
+@pytest.mark.parametrize("name,T", [("ragged_shared", 8), ("fs_narrow", 8), ("k3_verify8", 8),
+                                    ("fs_routed_2048", 40), ("k3_verify8", 40)])
+def test_batched_graph_replay_matches_eager(name, T):
     """A batched layer captured in a HIP graph and replayed with new inputs
     copied in between equals the eager call bit for bit, every replay.  At
     the K3 shape this covers the unrolled gate/up and the unit-stream down
-    kernels; the small shape the generic loops."""
+    kernels; the small shapes the generic loops.  Above 16 tokens: the
+    two-tile gate/up passes and the down kernel's pass tables (written by
+    the grouping kernel in every call)."""
     t = torch()
     w = SMALL[name] if name in SMALL else G.WORKLOADS[name]
     dl = device_layer(w, 0)
-    T = 8
     batches = [tokens_of(w, dl, T, start=1000 + 50 * i) for i in range(3)]
     ws = workspace(w, T)
     x = dev_u16(batches[0])
