@@ -23,6 +23,12 @@ Measurement
   first ~10 ms of replays run up to ~12 % slower than the steady state (the
   GPU's clocks and power state adjust), which a short timed region would
   otherwise measure instead of the layer.  The JSON reports the settle work.
+  One more untimed replay is enqueued right before the event that opens
+  the timed region, with no synchronisation in between: after a
+  synchronisation the stream is idle, so the opening event would fire at
+  once and the timed region would also hold the host's submission of the
+  graph and a cold start (measured: a single timed 20-step replay ran 0.2 to
+  1.5 us per layer above the replays that followed it).
 * Kernel pass: the same rotation through moe_decode_layer_timed, which
   launches the same kernels with HIP recording each kernel's own start and
   end; it gives the kernels per layer, their mean durations, the idle time
@@ -319,6 +325,9 @@ def main():
             settle_steps += 4 * (rep_steps if g_full is not None else rem)
             torch.cuda.synchronize()
         settle = {"steps": settle_steps, "seconds": round(time.perf_counter() - t_settle, 3)}
+        # one more untimed replay right before the opening event, with no
+        # synchronisation in between (see the module docstring)
+        g_settle.replay()
         evs[0].record(stream)
         for r in range(full):
             g_full.replay()
@@ -346,6 +355,7 @@ def main():
         if len(per_rep) < 8 and g_full is not None:
             extra = [torch.cuda.Event(enable_timing=True) for _ in range(33)]
             torch.cuda.synchronize()
+            g_full.replay()  # untimed lead, as for the timed replays
             extra[0].record(stream)
             for r in range(32):
                 g_full.replay()
