@@ -328,6 +328,7 @@ def main():
         # one more untimed replay right before the opening event, with no
         # synchronisation in between (see the module docstring)
         g_settle.replay()
+        settle["lead_steps"] = rep_steps if g_full is not None else rem
         evs[0].record(stream)
         for r in range(full):
             g_full.replay()
