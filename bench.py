@@ -118,9 +118,13 @@ def measured_traffic(workload: str, kernel_key: str):
     if not path or not os.path.exists(path):
         return None
     vals, table = P.read_counter_summary(path)
-    if vals.get("kernel_source_sha256_16") != P.source_digest():
-        return None
-    if kernel_key.startswith("kb_") and vals.get("batched_source_sha256_16") != P.source_digest(P.BATCHED_SRC):
+    # A kernel's bytes depend on its own source file (and the shared headers):
+    # the kb_* kernels on the batched file, the others on the one-token file.
+    if kernel_key.startswith("kb_"):
+        field, src = "batched_source_sha256_16", P.BATCHED_SRC
+    else:
+        field, src = "kernel_source_sha256_16", P.KERNEL_SRC
+    if vals.get(field) != P.source_digest(src):
         return None
     return table.get(kernel_key)
 
