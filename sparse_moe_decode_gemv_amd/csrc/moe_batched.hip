@@ -66,14 +66,18 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
-// Inclusive scan over a workgroup of kGroupBlock threads (16 waves).
-__device__ __forceinline__ int block_incl_scan(int v, int* wsum) {
+// Inclusive scan over a workgroup of kGroupBlock threads (16 waves).  The
+// wave totals are read back all at once and masked, rather than in a loop of
+// wid dependent LDS reads (the last wave's 15 reads were most of a scan).
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum) {
+  constexpr int NW = kGroupBlock / kWave;
   const int lane = threadIdx.x & 63, wid = wave_id();
-  const int inc = (int)wave_incl_scan_u32((uint32_t)v);
+  const uint32_t inc = wave_incl_scan_u32(v);
   if (lane == kWave - 1) wsum[wid] = inc;
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wid; ++w) before += wsum[w];
+  uint32_t before = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) before += w < wid ? wsum[w] : 0u;
   __syncthreads();
   return before + inc;
 }
@@ -134,19 +138,41 @@ __global__ __launch_bounds__(kBlk) void kb_router(LayerTB L, int n_et) {
 }
 
 // ---------------------------------------------------------------- top-k
+// V4 (E % 4 == 0): thread t requests experts 4 t .. 4 t + 3 of every split
+// as one 16-byte load (a wave's request is 1 KB contiguous), and wave 0 reads
+// its lanes' 16 logits back as four 16-byte LDS reads.  Scalar loads at a
+// 16-byte lane stride cost a vector-memory instruction per expert and split,
+// and 16 scalar LDS reads at a 64-byte lane stride conflict on the banks.
+template <bool V4>
 __global__ __launch_bounds__(kTopkBlock) void kb_topk(LayerTB L) {
+  static_assert(kTopkPerThread == 4, "a thread's four logits are one 16-byte piece");
   __shared__ TopkLds tk;
+  __shared__ __align__(16) float lg_lds[kMaxExperts];
   const int t = blockIdx.x;
   // all partial loads first (split index clamped, extra splits ignored), then
   // the sums in split order
   float v[kMaxRouterSplits][kTopkPerThread];
+  const int e0 = threadIdx.x * kTopkPerThread;
+  if constexpr (V4) {
+    const int eb = e0 + 4 <= L.E ? e0 : L.E - 4;  // in bounds; threads past E are ignored
 #pragma unroll
-  for (int ks = 0; ks < kMaxRouterSplits; ++ks) {
-    const int kc = ks < L.KS ? ks : L.KS - 1;
+    for (int ks = 0; ks < kMaxRouterSplits; ++ks) {
+      const int kc = ks < L.KS ? ks : L.KS - 1;
+      const float4 f = *reinterpret_cast<const float4*>(L.part + ((size_t)kc * L.T + t) * L.E + eb);
+      v[ks][0] = f.x;
+      v[ks][1] = f.y;
+      v[ks][2] = f.z;
+      v[ks][3] = f.w;
+    }
+  } else {
 #pragma unroll
-    for (int i = 0; i < kTopkPerThread; ++i) {
-      const int e = threadIdx.x * kTopkPerThread + i;
-      v[ks][i] = L.part[((size_t)kc * L.T + t) * L.E + (e < L.E ? e : L.E - 1)];
+    for (int ks = 0; ks < kMaxRouterSplits; ++ks) {
+      const int kc = ks < L.KS ? ks : L.KS - 1;
+#pragma unroll
+      for (int i = 0; i < kTopkPerThread; ++i) {
+        const int e = e0 + i;
+        v[ks][i] = L.part[((size_t)kc * L.T + t) * L.E + (e < L.E ? e : L.E - 1)];
+      }
     }
   }
   float lg[kTopkPerThread];
@@ -156,22 +182,25 @@ __global__ __launch_bounds__(kTopkBlock) void kb_topk(LayerTB L) {
 #pragma unroll
     for (int ks = 0; ks < kMaxRouterSplits; ++ks) s += ks < L.KS ? v[ks][i] : 0.f;
     lg[i] = s;
-    const int e = threadIdx.x * kTopkPerThread + i;
+    const int e = e0 + i;
     if (L.logits_out && e < L.E) L.logits_out[(size_t)t * L.E + e] = s;
   }
   // the selection by one wave (as for a single token): logits through LDS,
   // lane l taking experts 16 l .. 16 l + 15; no barrier inside
-  __shared__ float lg_lds[kMaxExperts];
-#pragma unroll
-  for (int i = 0; i < kTopkPerThread; ++i) lg_lds[threadIdx.x * kTopkPerThread + i] = lg[i];
+  *reinterpret_cast<float4*>(&lg_lds[e0]) = make_float4(lg[0], lg[1], lg[2], lg[3]);
   __syncthreads();
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     uint32_t key[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int e = 16 * lane + m;
-      key[m] = e < L.E ? f32_order_key(lg_lds[e]) : 0u;
+    for (int j = 0; j < 4; ++j) {
+      const float4 f = *reinterpret_cast<const float4*>(&lg_lds[16 * lane + 4 * j]);
+      const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // a mask, not a branch, so the reads stay 16 bytes wide
+        const int e = 16 * lane + 4 * j + i;
+        key[4 * j + i] = f32_order_key(fv[i]) & (0u - (uint32_t)(e < L.E));
+      }
     }
     const size_t o = (size_t)t * L.k;
     int32_t* io = L.idx_out ? L.idx_out + o : nullptr;
@@ -189,27 +218,40 @@ __global__ __launch_bounds__(kTopkBlock) void kb_topk(LayerTB L) {
 // within a token the grouping is unspecified, but every position stays in
 // bounds.)
 __global__ __launch_bounds__(kGroupBlock) void kb_group(LayerTB L) {
+  constexpr int PPT = (kMaxTokens * kMaxTopK + kGroupBlock - 1) / kGroupBlock;  // pairs per thread
   __shared__ uint32_t s_mask[kMaxExperts][2];
   __shared__ int s_off[kMaxExperts];
-  __shared__ int s_wsum[kGroupBlock / kWave];
+  __shared__ __align__(16) uint32_t s_wsum[kGroupBlock / kWave];
   const int tid = threadIdx.x;
   const int P = L.T * L.k;
   s_mask[tid][0] = 0u;
   s_mask[tid][1] = 0u;
+  // this thread's pairs tid, tid + kGroupBlock, ...: their experts stay in
+  // registers for the placement below
+  int pe[PPT];
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int p = tid + j * kGroupBlock;
+    const int e = p < P ? L.idx[p] : 0;
+    pe[j] = e < 0 ? 0 : (e >= L.E ? L.E - 1 : e);
+  }
   __syncthreads();
-  for (int p = tid; p < P; p += kGroupBlock) {
-    int e = L.idx[p];
-    e = e < 0 ? 0 : (e >= L.E ? L.E - 1 : e);
-    const int t = p / L.k;
-    atomicOr(&s_mask[e][t >> 5], 1u << (t & 31));
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int p = tid + j * kGroupBlock;
+    if (p < P) {
+      const int t = p / L.k;
+      atomicOr(&s_mask[pe[j]][t >> 5], 1u << (t & 31));
+    }
   }
   __syncthreads();
   const int cnt = tid < L.E ? __popc(s_mask[tid][0]) + __popc(s_mask[tid][1]) : 0;
   const int act = cnt > 0 ? 1 : 0;
   const int npass = (cnt + 15) / 16;  // passes of at most 16 pairs
-  const int off_incl = block_incl_scan(cnt, s_wsum);
-  const int act_incl = block_incl_scan(act, s_wsum);
-  const int pass_incl = block_incl_scan(npass, s_wsum);
+  // pair offsets (<= 2048) and active-group counts (<= 1024) in one scan
+  const uint32_t oa = block_incl_scan((uint32_t)cnt | ((uint32_t)act << 16), s_wsum);
+  const int off_incl = (int)(oa & 0xFFFFu), act_incl = (int)(oa >> 16);
+  const int pass_incl = (int)block_incl_scan((uint32_t)npass, s_wsum);
   const int off = off_incl - cnt;
   s_off[tid] = off;
   if (act) {
@@ -244,18 +286,21 @@ __global__ __launch_bounds__(kGroupBlock) void kb_group(LayerTB L) {
     if (L.offsets_out) L.offsets_out[L.E] = off_incl;
   }
   __syncthreads();
-  for (int p = tid; p < P; p += kGroupBlock) {
-    int e = L.idx[p];
-    e = e < 0 ? 0 : (e >= L.E ? L.E - 1 : e);
-    const int t = p / L.k;
-    const uint32_t m0 = s_mask[e][0], m1 = s_mask[e][1];
-    const int below = t < 32 ? __popc(m0 & ((1u << t) - 1u))
-                             : __popc(m0) + __popc(m1 & ((1u << (t - 32)) - 1u));
-    int pos = s_off[e] + below;
-    pos = pos < P ? pos : P - 1;
-    L.order[pos] = p;
-    L.pos_of[p] = pos;
-    if (L.pairs_out) L.pairs_out[pos] = p;
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int p = tid + j * kGroupBlock;
+    if (p < P) {
+      const int e = pe[j];
+      const int t = p / L.k;
+      const uint32_t m0 = s_mask[e][0], m1 = s_mask[e][1];
+      const int below = t < 32 ? __popc(m0 & ((1u << t) - 1u))
+                               : __popc(m0) + __popc(m1 & ((1u << (t - 32)) - 1u));
+      int pos = s_off[e] + below;
+      pos = pos < P ? pos : P - 1;
+      L.order[pos] = p;
+      L.pos_of[p] = pos;
+      if (L.pairs_out) L.pairs_out[pos] = p;
+    }
   }
   if (L.S)
     for (int t = tid; t < L.T; t += kGroupBlock) L.order[P + t] = P + t;
@@ -760,7 +805,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
 
   struct Unit {
     Tile D;
-    uint32_t voc, vos, xvo;
+    uint32_t voc, xvo;
     int pair0, m, n0, rt;
     bool live;
   };
@@ -775,7 +820,7 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
     u.rt = sb * kDnWaves + wid;
     const size_t row0 = (sh ? 0 : (size_t)e * L.H) + (size_t)u.rt * kTileRows;
     u.D = make_tile(sh ? L.sd_codes : L.d_codes, sh ? L.sd_scales : L.d_scales, row0, L.F);
-    tile_offsets<KC>(u.D, q, r, u.voc, u.vos);
+    u.voc = (uint32_t)r * u.D.rowc + 16u * (uint32_t)q;  // codes of block q of row r (scales: below)
     const int cs = n0 + sc < m ? n0 + sc : m - 1;
     u.xvo = (uint32_t)(start + cs - L.pos0) * (uint32_t)L.F * 2u + 16u * (uint32_t)sj;
     u.pair0 = start + n0;
@@ -985,7 +1030,10 @@ hipError_t launch_router_tb(const LayerTB& L, hipStream_t s) {
 }
 
 hipError_t launch_topk_tb(const LayerTB& L, hipStream_t s) {
-  MOE_LAUNCH(L.timer, kb_topk, dim3(L.T), dim3(kTopkBlock), 0, s, L);
+  if (L.E % 4 == 0)
+    MOE_LAUNCH(L.timer, kb_topk<true>, dim3(L.T), dim3(kTopkBlock), 0, s, L);
+  else
+    MOE_LAUNCH(L.timer, kb_topk<false>, dim3(L.T), dim3(kTopkBlock), 0, s, L);
   return hipPeekAtLastError();
 }
 

@@ -39,6 +39,9 @@ SMALL = {
                                  seed=0x5EED0208),
     "fs_shared_2048": G.Workload("fs_shared_2048", T=1, H=768, E=20, k=3, F=256, S=1, Fs=2048,
                                  seed=0x5EED0209),
+    # an expert count that is not a multiple of four: the top-k kernel then
+    # requests the router's partial sums one expert at a time
+    "odd_e": G.Workload("odd_e_b", T=1, H=512, E=37, k=5, F=256, S=1, Fs=256, seed=0x5EED020A),
 }
 
 
