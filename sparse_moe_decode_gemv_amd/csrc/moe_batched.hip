@@ -881,21 +881,25 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
 // Workgroup (token t, chunk of 8 kBlk hidden elements); each thread adds its
 // 8 elements over the slots in order, then the shared output and the
 // residual, and rounds once to bf16.
+//
+// KB > 0 (k == KB): every slot's rows, the shared row and the residual are
+// requested before the first addition, so a thread waits for one memory
+// round trip; the shared row and the residual come through descriptors that
+// are empty when absent.  KB == 0 (any k): whole batches of kCombineBatch
+// slots request their rows together, the remaining slots go one at a time.
+// The additions are in the same order either way.
+template <int KB>
 __global__ __launch_bounds__(kBlk) void kb_combine(LayerTB L) {
   const int t = blockIdx.x;
   const int h0 = (blockIdx.y * kBlk + threadIdx.x) * 8;
   if (h0 >= L.H) return;
   const int P = L.T * L.k;
   const int npos = P + L.S * L.T;
+  const size_t o = (size_t)t * L.H + h0;
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  // The token's weights and pair positions are workgroup-uniform (scalar
-  // loads).  Whole batches of kCombineBatch slots request their rows
-  // together, then add them in slot order; the remaining slots (k not a
-  // multiple of the batch) go one at a time.  Same order of additions either
-  // way.
-  constexpr int kCombineBatch = 8;
+  // the token's weights and pair positions are workgroup-uniform (scalar loads)
   const float* wt = L.wts + (size_t)t * L.k;
   const int32_t* pt = L.pos_of + (size_t)t * L.k;
   auto row_of = [&](int j) {
@@ -908,38 +912,60 @@ __global__ __launch_bounds__(kBlk) void kb_combine(LayerTB L) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(w, v[i], acc[i]);
   };
-  int j0 = 0;
-  for (; j0 + kCombineBatch <= L.k; j0 += kCombineBatch) {
-    float4 ya[kCombineBatch], yb[kCombineBatch];
-#pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) {
-      const float4* yp = row_of(j0 + u);
-      ya[u] = yp[0];
-      yb[u] = yp[1];
-    }
-#pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) add(ld_uniform(wt + j0 + u), ya[u], yb[u]);
-  }
-  for (int j = j0; j < L.k; ++j) {
-    const float4* yp = row_of(j);
-    add(ld_uniform(wt + j), yp[0], yp[1]);
-  }
-  if (L.S) {
-    const float4* yp = reinterpret_cast<const float4*>(L.y + (size_t)(P + t) * L.H + h0);
-    const float4 a = yp[0], b = yp[1];
+  auto add_shared = [&](const float4& a, const float4& b) {
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += v[i];
-  }
-  const size_t o = (size_t)t * L.H + h0;
-  if (L.residual) {
-    const uint4 rv = *reinterpret_cast<const uint4*>(L.residual + o);
+  };
+  auto add_residual = [&](const uint4& rv) {
     const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       acc[2 * d] += bf16_to_f32(rw[d] & 0xFFFFu);
       acc[2 * d + 1] += bf16_to_f32(rw[d] >> 16);
     }
+  };
+  if constexpr (KB > 0) {
+    float4 ya[KB], yb[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const float4* yp = row_of(u);
+      ya[u] = yp[0];
+      yb[u] = yp[1];
+    }
+    const uint32_t so = 4u * (uint32_t)((size_t)(P + t) * L.H + h0);
+    const auto rs = buf_rsrc(L.y, L.S ? 4u * (uint32_t)npos * (uint32_t)L.H : 0u);
+    const auto rr = buf_rsrc(L.residual, L.residual ? 2u * (uint32_t)L.T * (uint32_t)L.H : 0u);
+    const uint4 sa = buf_ld16(rs, so, 0u), sb = buf_ld16(rs, so + 16u, 0u);
+    const uint4 rv = buf_ld16(rr, 2u * (uint32_t)o, 0u);
+    __builtin_amdgcn_sched_barrier(0);  // every request above issued before the first addition
+#pragma unroll
+    for (int u = 0; u < KB; ++u) add(ld_uniform(wt + u), ya[u], yb[u]);
+    if (L.S) add_shared(__builtin_bit_cast(float4, sa), __builtin_bit_cast(float4, sb));
+    if (L.residual) add_residual(rv);
+  } else {
+    constexpr int kCombineBatch = 8;
+    int j0 = 0;
+    for (; j0 + kCombineBatch <= L.k; j0 += kCombineBatch) {
+      float4 ya[kCombineBatch], yb[kCombineBatch];
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) {
+        const float4* yp = row_of(j0 + u);
+        ya[u] = yp[0];
+        yb[u] = yp[1];
+      }
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) add(ld_uniform(wt + j0 + u), ya[u], yb[u]);
+    }
+    for (int j = j0; j < L.k; ++j) {
+      const float4* yp = row_of(j);
+      add(ld_uniform(wt + j), yp[0], yp[1]);
+    }
+    if (L.S) {
+      const float4* yp = reinterpret_cast<const float4*>(L.y + (size_t)(P + t) * L.H + h0);
+      add_shared(yp[0], yp[1]);
+    }
+    if (L.residual) add_residual(*reinterpret_cast<const uint4*>(L.residual + o));
   }
   uint32_t ow[4];
 #pragma unroll
@@ -1082,7 +1108,10 @@ hipError_t launch_down_tb(const LayerTB& L, hipStream_t s) {
 
 hipError_t launch_combine_tb(const LayerTB& L, hipStream_t s) {
   const int chunks = (L.H + 8 * kBlk - 1) / (8 * kBlk);
-  MOE_LAUNCH(L.timer, kb_combine, dim3(L.T, chunks), dim3(kBlk), 0, s, L);
+  if (L.k == 16)
+    MOE_LAUNCH(L.timer, kb_combine<16>, dim3(L.T, chunks), dim3(kBlk), 0, s, L);
+  else
+    MOE_LAUNCH(L.timer, kb_combine<0>, dim3(L.T, chunks), dim3(kBlk), 0, s, L);
   return hipPeekAtLastError();
 }
 

@@ -42,6 +42,12 @@ SMALL = {
     # an expert count that is not a multiple of four: the top-k kernel then
     # requests the router's partial sums one expert at a time
     "odd_e": G.Workload("odd_e_b", T=1, H=512, E=37, k=5, F=256, S=1, Fs=256, seed=0x5EED020A),
+    # top-16, the case whose combine requests every slot's rows at once: with
+    # and without a shared expert
+    "k16_shared": G.Workload("k16_shared_b", T=1, H=512, E=40, k=16, F=256, S=1, Fs=256,
+                             seed=0x5EED020B),
+    "k16_noshared": G.Workload("k16_noshared_b", T=1, H=512, E=40, k=16, F=256, S=0, Fs=0,
+                               seed=0x5EED020C),
 }
 
 
@@ -149,6 +155,31 @@ def test_router_topk_batched(name, T):
 @pytest.mark.parametrize("T", [2, 5, 17, 64])
 def test_batched_small_shapes(name, T):
     batched_parity(SMALL[name], T)
+
+
+@pytest.mark.parametrize("name", ["ragged_shared", "k16_shared", "k16_noshared"])
+def test_batched_no_residual_and_in_place_output(name):
+    """Residual absent (the combine adds none), then the residual buffer as
+    the output (in place); both against the oracle."""
+    t = torch()
+    w = SMALL[name]
+    T = 5
+    dl = device_layer(w, 0)
+    X = tokens_of(w, dl, T, start=30)
+    R = np.stack([G.token(w, 900 + i) for i in range(T)])
+    ref0 = oracle_layer(w, 0, dl.router_host, X, None)
+    ref1 = oracle_layer(w, 0, dl.router_host, X, R)
+    x = dev_u16(X)
+    ws = workspace(w, T)
+    out = t.empty_like(x)
+    M.decode_layer(shape_of(w), weights_of(dl), x, None, out, T, None, None, ws)
+    res = dev_u16(R)
+    M.decode_layer(shape_of(w), weights_of(dl), x, res, res, T, None, None, ws)  # in place
+    t.cuda.synchronize()
+    o0, o1 = host_u16(out), host_u16(res)
+    for i in range(T):
+        assert max_err_ratio(o0[i], ref0["out"][i])[0] <= TOL, (name, i)
+        assert max_err_ratio(o1[i], ref1["out"][i])[0] <= TOL, (name, i)
 
 
 @pytest.mark.parametrize("name", ["ragged_shared", "h8192"])
