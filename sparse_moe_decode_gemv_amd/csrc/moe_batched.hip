@@ -488,6 +488,42 @@ __device__ __forceinline__ void gu_load_a(GuRegs<KC>& R, const Tile& G, const Ti
   }
 }
 
+// Wide requests (one-tile gate/up at 512-element chunks): a wave instruction
+// reads 4 rows x 256 bytes of the tile (lane l: row 4 kk + l / 16, bytes
+// 16 (l % 16) of the chunk), nontemporal, instead of the operand layout's 16
+// rows x 64 bytes.  A streaming probe of the two shapes reads 7.0 against
+// 6.3 TB/s.  to_operand then moves the chunk to the operand layout through
+// a wave-private LDS tile (rows padded to 272 bytes: both the row-wise
+// stores and the column-wise loads hit distinct banks), so that lane (q, r)
+// holds bytes 64 kk + 16 q of row r, as ld_codes would have loaded them.
+template <int KC>
+__device__ __forceinline__ void ld_codes_wide(uint4 (&a)[KC / 128], const Tile& T, int c, int nch) {
+  static_assert(KC == 512, "a chunk is 256 bytes of each of the 16 rows");
+  const int lane = threadIdx.x & 63;
+  const bool live = c < nch;
+  const uint32_t cc = (uint32_t)(live ? c : nch - 1);
+  const auto rc = buf_rsrc(T.c, live ? 16u * T.rowc : 0u);
+  const uint32_t vo = (uint32_t)(lane >> 4) * T.rowc + 16u * (uint32_t)(lane & 15);
+#pragma unroll
+  for (int kk = 0; kk < KC / 128; ++kk) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(vo + 4u * kk * T.rowc), (int)(cc * (KC / 2)), kBufNT);
+    a[kk] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+constexpr int kWideRow = 17;  // uint4 per LDS row: 16 blocks + 16 bytes of padding
+// (The loads read other lanes' stores: wavefront-scope fences keep every
+// store before every load, and every load before the next chunk's stores.)
+template <int KC>
+__device__ __forceinline__ void to_operand(uint4 (&a)[KC / 128], uint4 (*slot)[kWideRow]) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int kk = 0; kk < KC / 128; ++kk) slot[4 * kk + q][r] = a[kk];
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+  for (int kk = 0; kk < KC / 128; ++kk) a[kk] = slot[r][4 * kk + q];
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+}
+
 // Products of one chunk: token tile 0 (LDS rows 0..15) always, tile 1 (rows
 // 16..31) when `two` (workgroup-uniform), from the same decoded fragments.
 template <int KC>
@@ -521,10 +557,13 @@ __device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, uint32_t sg, uint32_
 // of the group.  The one-tile and two-tile passes are separate code paths,
 // chosen per pass, so neither carries the other's requests.  With NCH > 0
 // the scales come from TS (requested once per item), else chunk by chunk.
-template <int KC, int NCH, bool TWO, class Lds>
+// WIDE: weights through ld_codes_wide and the wave's LDS tiles wt[0] (gate)
+// and wt[1] (up); NCH > 0 and one token tile only.
+template <int KC, int NCH, bool TWO, bool WIDE, class Lds>
 __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G, const Tile& U,
                                         const TileScales<NCH>& TS, uint32_t voc, uint32_t vos, int start,
-                                        int m, int n0, int rq) {
+                                        int m, int n0, int rq, uint4 (*wt)[16][kWideRow]) {
+  static_assert(!WIDE || (NCH > 0 && !TWO), "wide requests: scales preloaded, one token tile");
   constexpr bool PRE = NCH > 0;
   constexpr int PER = KC / 128;  // staged uint4 per thread per chunk and tile
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
@@ -541,17 +580,25 @@ __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G,
   const auto rw0 = 4 * wid < m - n0 ? rx : rx0, rw1 = 16 + 4 * wid < m - n0 ? rx : rx0;
   f32x4 cg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   f32x4 cu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  auto load_w = [&](GuRegs<KC>& A, int c) {
+    if constexpr (WIDE) {
+      ld_codes_wide<KC>(A.ag, G, c, nch);
+      ld_codes_wide<KC>(A.au, U, c, nch);
+    } else {
+      gu_load_a<KC, PRE>(A, G, U, voc, vos, c, nch);
+    }
+  };
   GuRegs<KC> A0, A1;
   Stage<PER> xa0, xa1, xb0, xb1;
   xa0.load(rw0, xv0, xso(0));
   if (TWO) xa1.load(rw1, xv1, xso(0));
   __builtin_amdgcn_sched_barrier(0);
-  gu_load_a<KC, PRE>(A0, G, U, voc, vos, 0, nch);
+  load_w(A0, 0);
   __builtin_amdgcn_sched_barrier(0);
   xb0.load(rw0, xv0, xso(1));
   if (TWO) xb1.load(rw1, xv1, xso(1));
   __builtin_amdgcn_sched_barrier(0);
-  gu_load_a<KC, PRE>(A1, G, U, voc, vos, 1, nch);
+  load_w(A1, 1);
   __builtin_amdgcn_sched_barrier(0);
   xa0.store(&S.b[0][sc][sj]);
   if (TWO) xa1.store(&S.b[0][16 + sc][sj]);
@@ -560,6 +607,10 @@ __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G,
   // weights and activations (xs) in flight; xl takes chunk c + 2's
   auto step = [&](int c, GuRegs<KC>& Ac, Stage<PER>& xl0, Stage<PER>& xl1, const Stage<PER>& xs0,
                   const Stage<PER>& xs1, const uint4 (*bu)[KC / 8 + 1], uint4 (*bs)[KC / 8 + 1]) {
+    if constexpr (WIDE) {
+      to_operand<KC>(Ac.ag, wt[0]);
+      to_operand<KC>(Ac.au, wt[1]);
+    }
     if constexpr (PRE)
       gu_mma<KC>(Ac, TS.g[c], TS.u[c], bu, q, r, TWO, cg, cu);
     else
@@ -568,7 +619,7 @@ __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G,
       xl0.load(rw0, xv0, xso(c + 2));
       if (TWO) xl1.load(rw1, xv1, xso(c + 2));
       __builtin_amdgcn_sched_barrier(0);
-      gu_load_a<KC, PRE>(Ac, G, U, voc, vos, c + 2, nch);
+      load_w(Ac, c + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (!NCH || c + 1 < nch) {
@@ -612,12 +663,18 @@ __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G,
   }
 }
 
+// One-tile passes (batches of at most 16 tokens) request their weights wide
+// (ld_codes_wide); the wave tiles take 34 KB of LDS, so two workgroups per CU.
+constexpr bool kGuWide = true;
+
 // MAXT: token tiles per pass (1 when no group can exceed 16 tokens: T <= 16,
 // which keeps the smaller LDS and one more workgroup per CU).
 template <int KC, int NCH, int MAXT>
 __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
   using Lds = typename std::conditional<MAXT == 2, TokLds2<KC>, TokLds<KC>>::type;
+  constexpr bool WIDE = kGuWide && MAXT == 1 && NCH > 0 && KC == 512;
   __shared__ Lds S;
+  __shared__ uint4 wtile[WIDE ? kWv : 1][2][16][kWideRow];  // per wave: gate, up
   const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
   int g0, g1;
   group_range(L, g0, g1);
@@ -639,9 +696,9 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
     }
     for (int n0 = 0; n0 < m; n0 += 16 * MAXT) {
       if (MAXT == 2 && m - n0 > 16)  // workgroup-uniform
-        gu_pass<KC, NCH, true>(L, S, G, U, TS, voc, vos, start, m, n0, rq);
+        gu_pass<KC, NCH, true, false>(L, S, G, U, TS, voc, vos, start, m, n0, rq, wtile[0]);
       else
-        gu_pass<KC, NCH, false>(L, S, G, U, TS, voc, vos, start, m, n0, rq);
+        gu_pass<KC, NCH, false, WIDE>(L, S, G, U, TS, voc, vos, start, m, n0, rq, wtile[WIDE ? wid : 0]);
     }
   }
 }
@@ -1042,7 +1099,7 @@ __global__ __launch_bounds__(kBlk) void kb_rmsnorm(const uint16_t* __restrict__ 
 // 256-element chunks three (147 registers, 33 KB).  One tile (T <= 16):
 // three with 512-element chunks (137 registers, 33 KB), four with 256 (109).
 constexpr int kGroupedBlocksPerCU[2] = {4, 3};     // 256-element chunks, by tiles - 1
-constexpr int kGroupedBlocksPerCU512[2] = {3, 2};  // 512-element chunks
+constexpr int kGroupedBlocksPerCU512[2] = {kGuWide ? 2 : 3, 2};  // 512-element chunks
 constexpr int kDownBlocksPerCU = 2;
 constexpr int kNumCUs = 256;
 
