@@ -488,14 +488,15 @@ __device__ __forceinline__ void gu_load_a(GuRegs<KC>& R, const Tile& G, const Ti
   }
 }
 
-// Wide requests (one-tile gate/up at 512-element chunks): a wave instruction
-// reads 4 rows x 256 bytes of the tile (lane l: row 4 kk + l / 16, bytes
-// 16 (l % 16) of the chunk), nontemporal, instead of the operand layout's 16
-// rows x 64 bytes.  A streaming probe of the two shapes reads 7.0 against
-// 6.3 TB/s.  to_operand then moves the chunk to the operand layout through
-// a wave-private LDS tile (rows padded to 272 bytes: both the row-wise
-// stores and the column-wise loads hit distinct banks), so that lane (q, r)
-// holds bytes 64 kk + 16 q of row r, as ld_codes would have loaded them.
+// Wide requests (one-tile gate/up passes at 512-element chunks): a wave
+// instruction reads 4 rows x 256 bytes of the tile (lane l: row 4 kk + l / 16,
+// bytes 16 (l % 16) of the chunk), nontemporal, instead of the operand
+// layout's 16 rows x 64 bytes.  A streaming probe of the two shapes reads
+// 7.0 against 6.3 TB/s.  to_operand then moves the chunk to the operand
+// layout through a wave-private LDS tile of 16 x 16 pieces of 16 bytes
+// (piece b of row R stored at R * 16 + (b ^ R): the row-wise stores and the
+// column-wise loads both hit distinct banks), so that lane (q, r) holds
+// bytes 64 kk + 16 q of row r, as ld_codes would have loaded them.
 template <int KC>
 __device__ __forceinline__ void ld_codes_wide(uint4 (&a)[KC / 128], const Tile& T, int c, int nch) {
   static_assert(KC == 512, "a chunk is 256 bytes of each of the 16 rows");
@@ -510,17 +511,20 @@ __device__ __forceinline__ void ld_codes_wide(uint4 (&a)[KC / 128], const Tile& 
     a[kk] = make_uint4(v[0], v[1], v[2], v[3]);
   }
 }
-constexpr int kWideRow = 17;  // uint4 per LDS row: 16 blocks + 16 bytes of padding
+constexpr int kWideTile = 256;  // uint4 per wave and matrix
 // (The loads read other lanes' stores: wavefront-scope fences keep every
 // store before every load, and every load before the next chunk's stores.)
 template <int KC>
-__device__ __forceinline__ void to_operand(uint4 (&a)[KC / 128], uint4 (*slot)[kWideRow]) {
+__device__ __forceinline__ void to_operand(uint4 (&a)[KC / 128], uint4* slot) {
   const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
 #pragma unroll
-  for (int kk = 0; kk < KC / 128; ++kk) slot[4 * kk + q][r] = a[kk];
+  for (int kk = 0; kk < KC / 128; ++kk) {
+    const int row = 4 * kk + q;  // stored: piece r of row 4 kk + q
+    slot[row * 16 + (r ^ row)] = a[kk];
+  }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
-  for (int kk = 0; kk < KC / 128; ++kk) a[kk] = slot[r][4 * kk + q];
+  for (int kk = 0; kk < KC / 128; ++kk) a[kk] = slot[r * 16 + ((4 * kk + q) ^ r)];
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 }
 
@@ -557,12 +561,12 @@ __device__ __forceinline__ void gu_mma(const GuRegs<KC>& R, uint32_t sg, uint32_
 // of the group.  The one-tile and two-tile passes are separate code paths,
 // chosen per pass, so neither carries the other's requests.  With NCH > 0
 // the scales come from TS (requested once per item), else chunk by chunk.
-// WIDE: weights through ld_codes_wide and the wave's LDS tiles wt[0] (gate)
-// and wt[1] (up); NCH > 0 and one token tile only.
+// WIDE: weights through ld_codes_wide and the wave's LDS tiles wt (gate)
+// and wt + kWideTile (up); NCH > 0 and one token tile only.
 template <int KC, int NCH, bool TWO, bool WIDE, class Lds>
 __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G, const Tile& U,
                                         const TileScales<NCH>& TS, uint32_t voc, uint32_t vos, int start,
-                                        int m, int n0, int rq, uint4 (*wt)[16][kWideRow]) {
+                                        int m, int n0, int rq, uint4* wt) {
   static_assert(!WIDE || (NCH > 0 && !TWO), "wide requests: scales preloaded, one token tile");
   constexpr bool PRE = NCH > 0;
   constexpr int PER = KC / 128;  // staged uint4 per thread per chunk and tile
@@ -608,8 +612,8 @@ __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G,
   auto step = [&](int c, GuRegs<KC>& Ac, Stage<PER>& xl0, Stage<PER>& xl1, const Stage<PER>& xs0,
                   const Stage<PER>& xs1, const uint4 (*bu)[KC / 8 + 1], uint4 (*bs)[KC / 8 + 1]) {
     if constexpr (WIDE) {
-      to_operand<KC>(Ac.ag, wt[0]);
-      to_operand<KC>(Ac.au, wt[1]);
+      to_operand<KC>(Ac.ag, wt);
+      to_operand<KC>(Ac.au, wt + kWideTile);
     }
     if constexpr (PRE)
       gu_mma<KC>(Ac, TS.g[c], TS.u[c], bu, q, r, TWO, cg, cu);
@@ -663,8 +667,9 @@ __device__ __forceinline__ void gu_pass(const LayerTB& L, Lds& S, const Tile& G,
   }
 }
 
-// One-tile passes (batches of at most 16 tokens) request their weights wide
-// (ld_codes_wide); the wave tiles take 34 KB of LDS, so two workgroups per CU.
+// One-tile passes request their weights wide (ld_codes_wide).  In the
+// one-tile kernel (batches of at most 16 tokens) the wave tiles take 32 KB
+// more LDS, so two workgroups per CU instead of three.
 constexpr bool kGuWide = true;
 
 // MAXT: token tiles per pass (1 when no group can exceed 16 tokens: T <= 16,
@@ -672,9 +677,12 @@ constexpr bool kGuWide = true;
 template <int KC, int NCH, int MAXT>
 __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
   using Lds = typename std::conditional<MAXT == 2, TokLds2<KC>, TokLds<KC>>::type;
-  constexpr bool WIDE = kGuWide && MAXT == 1 && NCH > 0 && KC == 512;
+  constexpr bool WIDE = kGuWide && NCH > 0 && KC == 512;  // one-tile passes
   __shared__ Lds S;
-  __shared__ uint4 wtile[WIDE ? kWv : 1][2][16][kWideRow];  // per wave: gate, up
+  // per wave: the gate and up tiles of the wide requests.  With two token
+  // tiles they take the second tile's staging rows, which one-tile passes
+  // leave unused (16 rows of 65 pieces in each buffer: two waves' tiles).
+  __shared__ uint4 wtile[WIDE && MAXT == 1 ? kWv : 1][2 * kWideTile];
   const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
   int g0, g1;
   group_range(L, g0, g1);
@@ -689,6 +697,9 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
     const Tile U = make_tile(sh ? L.su_codes : L.u_codes, sh ? L.su_scales : L.u_scales, row0, L.H);
     uint32_t voc, vos;
     tile_offsets<KC>(G, q, r, voc, vos);
+    uint4* const wt = !WIDE ? nullptr
+                      : MAXT == 1 ? wtile[wid]
+                                  : &S.b[wid >> 1][16][0] + (wid & 1) * (2 * kWideTile);
     TileScales<NCH> TS;
     if constexpr (NCH > 0) {
       ld_scales<KC, NCH>(TS.g, G, vos);
@@ -696,9 +707,9 @@ __global__ __launch_bounds__(kBlk) void kb_gateup(LayerTB L) {
     }
     for (int n0 = 0; n0 < m; n0 += 16 * MAXT) {
       if (MAXT == 2 && m - n0 > 16)  // workgroup-uniform
-        gu_pass<KC, NCH, true, false>(L, S, G, U, TS, voc, vos, start, m, n0, rq, wtile[0]);
+        gu_pass<KC, NCH, true, false>(L, S, G, U, TS, voc, vos, start, m, n0, rq, nullptr);
       else
-        gu_pass<KC, NCH, false, WIDE>(L, S, G, U, TS, voc, vos, start, m, n0, rq, wtile[WIDE ? wid : 0]);
+        gu_pass<KC, NCH, false, WIDE>(L, S, G, U, TS, voc, vos, start, m, n0, rq, wt);
     }
   }
 }
