@@ -512,8 +512,9 @@ __device__ __forceinline__ void ld_codes_wide(uint4 (&a)[KC / 128], const Tile& 
   }
 }
 constexpr int kWideTile = 256;  // uint4 per wave and matrix
-// (The loads read other lanes' stores: wavefront-scope fences keep every
-// store before every load, and every load before the next chunk's stores.)
+// (The loads read other lanes' stores: a wavefront-scope fence keeps every
+// store before every load.  The next chunk's stores come after the barrier
+// that ends the chunk, which already orders them after these loads.)
 template <int KC>
 __device__ __forceinline__ void to_operand(uint4 (&a)[KC / 128], uint4* slot) {
   const int lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
@@ -525,7 +526,6 @@ __device__ __forceinline__ void to_operand(uint4 (&a)[KC / 128], uint4* slot) {
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
   for (int kk = 0; kk < KC / 128; ++kk) a[kk] = slot[r * 16 + ((4 * kk + q) ^ r)];
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 }
 
 // Products of one chunk: token tile 0 (LDS rows 0..15) always, tile 1 (rows
