@@ -945,6 +945,145 @@ __global__ __launch_bounds__(kDnBlock) void kb_down_flat(LayerTB L) {
   }
 }
 
+// The FFN-2048 down kernel for batches of at most 8 tokens (no group holds
+// more than 8 pairs, so a unit is a whole group): kb_down_flat's units and
+// chunk stream, with
+//  - 8 staged pair rows instead of 16 (16 KB of LDS per part instead of 33),
+//    pieces swizzled instead of padded (piece p of row R at p ^ R), and
+//  - the weights requested wide (ld_codes_wide: 4 rows x 256 B per wave
+//    instruction, nontemporal) and moved to the operand layout through a
+//    4 KB LDS tile per wave (to_operand), which the freed LDS holds.
+// Operand columns 8..15 read the rows of columns 0..7 again (an LDS
+// broadcast); their results are not stored.
+template <int KC>
+struct TokLdsSw8 {
+  uint4 b[2][8][KC / 8];
+};
+template <int KC>
+__device__ __forceinline__ void dn_mma_w8(const DnRegs<KC>& R, const uint4 (*bh)[KC / 8],
+                                          const uint4 (*bl)[KC / 8], int q, int r, f32x4& acc,
+                                          const u32x4& quad, int c) {
+  const int r8 = r & 7;
+#pragma unroll
+  for (int kk = 0; kk < KC / 128; ++kk) {
+    const float f = e8m0_to_f32(byte_of((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (16 * c + r), (int)quad[kk]), q));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 av = fp4x8_to_bf16(dword_of(R.a[kk], s), f);
+      acc = mfma16(av, as_bf16x8(bh[r8][kk * 16 + ((4 * q + s) ^ r8)]), acc);
+      acc = mfma16(av, as_bf16x8(bl[r8][kk * 16 + ((4 * q + s) ^ r8)]), acc);
+    }
+  }
+}
+// A thread's two staged pieces of one pair row (32 threads a row, pieces
+// j and j + 32).
+struct Stage8 {
+  u32x4 v[2];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 512u * i), (int)soff, 0));
+  }
+  __device__ __forceinline__ void store(uint4* dst) const {  // dst: the thread's first piece
+    u32x4* p = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) p[32 * i] = v[i];
+  }
+};
+
+template <int KC, int NCH>
+__global__ __launch_bounds__(kDnBlock) void kb_down_w8(LayerTB L) {
+  static_assert(NCH == 4 && KC == 512, "a unit's scales are one 16-byte piece per lane (q, r)");
+  __shared__ TokLdsSw8<KC> Sh, Sl;
+  __shared__ uint4 dtile[kDnWaves][kWideTile];  // the waves' wide-request tiles
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15, wid = wave_id();
+  int v0, v1;
+  group_range(L, v0, v1);
+  const int slabs = L.H / (kTileRows * kDnWaves);
+  const int nitems = (v1 - v0) * slabs;
+  // staging: waves 0..3 stage a_hi, 4..7 a_lo; thread row sc (0..7), pieces sj, sj + 32
+  const bool st_lo = wid >= kDnWaves / 2;
+  const int sc = (tid & 255) >> 5, sj = tid & 31;
+  const uint32_t npairs = (uint32_t)(L.T * L.k + L.S * L.T);
+  const uint32_t nrows = act_rows(L);
+  const uint16_t* abase = st_lo ? L.act_lo : L.act_hi;
+  const auto ra = buf_rsrc(abase, nrows * (uint32_t)L.F * 2u), ra0 = buf_rsrc(abase, 0u);
+  const auto ry = buf_rsrc(L.y, npairs * (uint32_t)L.H * 4u);
+  uint4 (*sbuf[2])[KC / 8] = {st_lo ? Sl.b[0] : Sh.b[0], st_lo ? Sl.b[1] : Sh.b[1]};
+  uint4* const tile = dtile[wid];
+
+  struct Unit {
+    Tile D;
+    uint32_t xvo;
+    int pair0, m, rt;
+    bool live;
+  };
+  auto unit_at = [&](int it) {
+    Unit u;
+    u.live = it < nitems;
+    const int itc = u.live ? it : nitems - 1;
+    const int vi = itc / slabs, sb = itc - vi * slabs, g = v0 + vi;
+    const int e = ld_uniform(L.g_expert + g), start = ld_uniform(L.g_start + g), m = ld_uniform(L.g_count + g);
+    const bool sh = e >= L.E;
+    u.rt = sb * kDnWaves + wid;
+    const size_t row0 = (sh ? 0 : (size_t)e * L.H) + (size_t)u.rt * kTileRows;
+    u.D = make_tile(sh ? L.sd_codes : L.d_codes, sh ? L.sd_scales : L.d_scales, row0, L.F);
+    const int cs = sc < m ? sc : m - 1;
+    u.xvo = (uint32_t)(start + cs - L.pos0) * (uint32_t)L.F * 2u + 16u * (uint32_t)sj;
+    u.pair0 = start;
+    u.m = m;
+    return u;
+  };
+  // a wave stages rows 2 (wid & 3) and 2 (wid & 3) + 1; when both are past
+  // the group's pairs it requests nothing (empty descriptor: zeros)
+  const int srow0 = 2 * (wid & 3);
+  auto load_chunk = [&](const Unit& u, int c, DnRegs<KC>& A, Stage8& X, u32x4& Q) {
+    X.load(u.live && srow0 < u.m ? ra : ra0, u.xvo, (uint32_t)c * (uint32_t)(KC * 2));
+    __builtin_amdgcn_sched_barrier(0);
+    ld_codes_wide<KC>(A.a, u.D, u.live ? c : NCH, NCH);
+    if (c == 0)  // the unit's scales: bytes 16 q .. 16 q + 15 of row r
+      Q = __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(u.D.s, u.live ? 16u * u.D.rows : 0u),
+                                                (int)(r * u.D.rows + 16u * (uint32_t)q), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int it = blockIdx.x;
+  if (it >= nitems) return;
+  Unit cur = unit_at(it);
+  DnRegs<KC> A0, A1;
+  Stage8 xa, xb;
+  u32x4 qc, qn;  // this unit's scales, the next unit's
+  load_chunk(cur, 0, A0, xa, qc);
+  load_chunk(cur, 1, A1, xb, qc);
+  xa.store(&sbuf[0][sc][sj ^ sc]);
+  __syncthreads();
+  for (;;) {
+    const Unit nxt = unit_at(it + (int)gridDim.x);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      DnRegs<KC>& Ac = (c & 1) ? A1 : A0;
+      Stage8& xl = (c & 1) ? xb : xa;
+      const Stage8& xs = (c & 1) ? xa : xb;
+      to_operand<KC>(Ac.a, tile);  // the chunk's closing barrier orders its loads before the next stores
+      dn_mma_w8<KC>(Ac, Sh.b[c & 1], Sl.b[c & 1], q, r, acc, qc, c);
+      if (c + 2 < NCH) load_chunk(cur, c + 2, Ac, xl, qc);
+      else load_chunk(nxt, c + 2 - NCH, Ac, xl, qn);
+      xs.store(&sbuf[(c + 1) & 1][sc][sj ^ sc]);
+      __syncthreads();
+    }
+    // columns of valid pairs only (the store's range check drops the others)
+    const bool ok = r < 8 && r < cur.m;
+    const uint32_t yo = ok ? 4u * ((uint32_t)(cur.pair0 + r) * (uint32_t)L.H + (uint32_t)(cur.rt * kTileRows + 4 * q))
+                           : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ry, (int)yo, 0, 0);
+    if (!nxt.live) break;
+    it += (int)gridDim.x;
+    cur = nxt;
+    qc = qn;  // waits for the next unit's first chunk, which its first products need anyway
+  }
+}
+
 // ---------------------------------------------------------------- combine
 // Workgroup (token t, chunk of 8 kBlk hidden elements); each thread adds its
 // 8 elements over the slots in order, then the shared output and the
@@ -1161,7 +1300,9 @@ hipError_t launch_gateup_tb(const LayerTB& L, hipStream_t s) {
 hipError_t launch_down_tb(const LayerTB& L, hipStream_t s) {
   const dim3 grid(kNumCUs * kDownBlocksPerCU);
   // a group holds at most T pairs: more than one pass only when T > 16
-  if (L.F == 2048 && L.T > 16)
+  if (L.F == 2048 && L.T <= 8)
+    MOE_LAUNCH(L.timer, (kb_down_w8<512, 4>), grid, dim3(kDnBlock), 0, s, L);
+  else if (L.F == 2048 && L.T > 16)
     MOE_LAUNCH(L.timer, (kb_down_flat<512, 4, true>), grid, dim3(kDnBlock), 0, s, L);
   else if (L.F == 2048)
     MOE_LAUNCH(L.timer, (kb_down_flat<512, 4, false>), grid, dim3(kDnBlock), 0, s, L);
