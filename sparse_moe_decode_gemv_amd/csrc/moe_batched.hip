@@ -23,7 +23,7 @@
 //  down     grouped GEMM per (group, 16-row tile of the hidden size) over
 //           a_hi and a_lo -> fp32 expert outputs per sorted pair; at FFN
 //           2048 each wave runs its units as one chunk stream
-//           (kb_down_flat).
+//           (kb_down_flat; kb_down_w8 for batches of at most 8 tokens).
 //  combine  per token: residual + sum_j w_j y_j (slot order) + y_shared ->
 //           bf16; fixed order, no floating-point atomics.
 //
@@ -34,12 +34,15 @@
 // section "四步改造"; the pages' fast path stops at 64 tokens: page "AI手搓
 // 1.2万行代码榨干GB300!…", section 03).  Weight bytes still dominate, so the
 // grouped kernels keep consecutive waves on consecutive row tiles of one
-// expert, request each chunk two chunks ahead with 16-byte buffer loads
-// through L2 (a request covers 64 bytes of a row, the next one the rest of
-// the line), request a tile's scales once per work item (chunk by chunk,
-// the weight stream evicted the scale lines between uses), and keep the
-// count of requests per chunk low (no staging requests for token rows past
-// the group).
+// expert, request each chunk two chunks ahead with 16-byte buffer loads,
+// request a tile's scales once per work item (chunk by chunk, the weight
+// stream evicted the scale lines between uses), and keep the count of
+// requests per chunk low (no staging requests for token rows past the
+// group).  The operand layout covers 64 bytes of each of 16 rows per wave
+// instruction (the next request completes the line through L2); where LDS
+// allows (one-tile gate/up passes, the down kernel at up to 8 tokens) the
+// weights are requested instead as 4 rows x 256 bytes, nontemporal, and
+// moved to the operand layout through a wave-private LDS tile.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 fragments (lane l = 16 q + r): A holds
 // A[r][8q .. 8q+7], B holds B[8q .. 8q+7][r], the result C[4q .. 4q+3][r].
