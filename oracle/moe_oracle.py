@@ -37,8 +37,9 @@ pages give no formulas; the definitions below are the plain readings:
 
 Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
 against hand-worked format tables, brute force on tiny inputs, closed forms
-and invariants.  Points where the pages are silent are listed with the
-reading taken in the design doc.
+and invariants.  Where the pages are silent, the readings taken are the
+ones stated in the steps above (stable top-k order, float64 accumulation,
+bf16 rounding only where a step says so).
 """
 from __future__ import annotations
 
